@@ -1,0 +1,279 @@
+"""Python binding of libmxattn.so (MXFP4 FlashAttention for MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP library.  torch tensors
+provide device memory and the current stream.  If the shared library is
+missing the import fails; there is no fallback path.
+
+    import bit_microscaled_flashattention_amd as mxa
+    qh = mxa.quantize(q)                        # [B,H,S,D] bf16 -> MXFP4 (HD)
+    vh = mxa.quantize(v, layout="key")          # 32-key blocks per channel
+    out = mxa.prefill(qh, kh, vh, causal=True)
+"""
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxattn.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, F16, BF16 = 0, 1, 2
+SCALE_OCP, SCALE_UOS = 0, 1
+LAYOUT_HD, LAYOUT_KEY = 0, 1
+UOS_QMAX = 7.25
+
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_RULES = {"ocp": SCALE_OCP, "uos": SCALE_UOS}
+
+
+class MxattnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"mxattn status {status}: {message}")
+        self.status = status
+
+
+class _Mx(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64),
+        ("seq", ctypes.c_int64), ("dim", ctypes.c_int64),
+        ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("code_stride", ctypes.c_int64 * 3), ("scale_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class _PrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("kv_tile", ctypes.c_int32), ("p_rule", ctypes.c_int32),
+        ("p_qmax", ctypes.c_float), ("l_from_quantized", ctypes.c_int32),
+    ]
+
+
+class _Hybrid(ctypes.Structure):
+    _fields_ = [
+        ("idx", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
+        ("max_sel", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("k_sel", ctypes.c_void_p), ("v_sel", ctypes.c_void_p),
+        ("k_win", ctypes.c_void_p), ("v_win", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m bit_microscaled_flashattention_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "mxattn_quantize": [vp, i32, P(i64), vp, i32, f32, P(_Mx), vp],
+        "mxattn_smooth_calibrate": [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp],
+        "mxattn_prefill": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), vp, i32, vp, vp],
+        "mxattn_decode": [P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
+        "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = i32
+    lib.mxattn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.mxattn_decode_workspace_bytes.restype = sz
+    lib.mxattn_select_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.mxattn_select_workspace_bytes.restype = sz
+    for name in ("mxattn_last_error", "mxattn_version"):
+        getattr(lib, name).restype = ctypes.c_char_p
+        getattr(lib, name).argtypes = []
+    lib.mxattn_status_string.restype = ctypes.c_char_p
+    lib.mxattn_status_string.argtypes = [i32]
+    return lib
+
+
+_lib = _load()
+
+# Every symbol the C header declares (checked by the CPU tests).
+EXPORTS = (
+    "mxattn_quantize", "mxattn_smooth_calibrate", "mxattn_prefill",
+    "mxattn_decode_workspace_bytes", "mxattn_decode",
+    "mxattn_select_workspace_bytes", "mxattn_select_vertical",
+    "mxattn_status_string", "mxattn_last_error", "mxattn_version",
+)
+
+
+def library():
+    return _lib
+
+
+def version():
+    return _lib.mxattn_version().decode()
+
+
+def _check(status):
+    if status != OK:
+        raise MxattnError(status, _lib.mxattn_last_error().decode())
+
+
+def _stream(t=None):
+    if t is not None and t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+@dataclass
+class MX:
+    """An MXFP4 tensor: packed E2M1 codes + E8M0 scale bytes (torch uint8).
+
+    layout "hd":  codes [B,H,S,D/2], scales [B,H,S,D/32]
+    layout "key": codes [B,H,D,ceil(S/32)*16], scales [B,H,D,ceil(S/32)]
+    """
+    codes: torch.Tensor
+    scales: torch.Tensor
+    shape: tuple
+    layout: str = "hd"
+
+    def desc(self):
+        b, h, s, d = self.shape
+        c, sc = self.codes, self.scales
+        m = _Mx()
+        m.codes, m.scales = c.data_ptr(), sc.data_ptr()
+        m.batch, m.heads, m.seq, m.dim = b, h, s, d
+        m.layout = LAYOUT_HD if self.layout == "hd" else LAYOUT_KEY
+        for i in range(3):
+            m.code_stride[i] = c.stride(i) * c.element_size()
+            m.scale_stride[i] = sc.stride(i) * sc.element_size()
+        return m
+
+    def narrow_seq(self, start, length):
+        """View of tokens [start, start+length) of an HD tensor (no copy)."""
+        assert self.layout == "hd"
+        b, h, _, d = self.shape
+        return MX(self.codes[:, :, start:start + length], self.scales[:, :, start:start + length],
+                  (b, h, length, d), "hd")
+
+
+def empty_mx(shape, layout="hd", device="cuda"):
+    b, h, s, d = shape
+    if layout == "hd":
+        codes = torch.empty((b, h, s, d // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((b, h, s, d // 32), dtype=torch.uint8, device=device)
+    else:
+        nb = (s + 31) // 32
+        codes = torch.empty((b, h, d, nb * 16), dtype=torch.uint8, device=device)
+        scales = torch.empty((b, h, d, nb), dtype=torch.uint8, device=device)
+    return MX(codes, scales, tuple(shape), layout)
+
+
+def quantize(x, layout="hd", chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None):
+    """MXFP4-encode x [B,H,S,D] (bf16/fp16/fp32, last dim contiguous)."""
+    assert x.dim() == 4 and x.stride(3) == 1, "x must be [B,H,S,D] with contiguous D"
+    if out is None:
+        out = empty_mx(tuple(x.shape), layout, x.device)
+    strides = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    cs = None
+    if chan_scale is not None:
+        cs = chan_scale.to(torch.float32).contiguous()
+    d = out.desc()
+    _check(_lib.mxattn_quantize(_ptr(x), _DT[x.dtype], strides, _ptr(cs), _RULES[rule],
+                                float(qmax), ctypes.byref(d), _stream(x)))
+    return out
+
+
+def smooth_calibrate(q_cal, k_cal):
+    """Smooth-QK factors from calibration slices q_cal [Hq,T,D], k_cal [Hkv,T,D]."""
+    q_cal, k_cal = q_cal.contiguous(), k_cal.contiguous()
+    hq, t, d = q_cal.shape
+    hkv = k_cal.shape[0]
+    qs = torch.empty((hq, d), dtype=torch.float32, device=q_cal.device)
+    ks = torch.empty((hkv, d), dtype=torch.float32, device=q_cal.device)
+    _check(_lib.mxattn_smooth_calibrate(_ptr(q_cal), _ptr(k_cal), _DT[q_cal.dtype], hq, hkv, t, d,
+                                        _ptr(qs), _ptr(ks), _stream(q_cal)))
+    return qs, ks
+
+
+def prefill(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, p_rule="ocp",
+            p_qmax=UOS_QMAX, l_from_quantized=True, out_dtype=torch.float32, return_lse=False,
+            out=None):
+    """MXFP4 attention forward; q, k: MX (hd), v: MX (key).  Returns out [B,Hq,Sq,D]."""
+    b, hq, sq, d = q.shape
+    if out is None:
+        out = torch.empty((b, hq, sq, d), dtype=out_dtype, device=q.codes.device)
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.codes.device) if return_lse else None
+    p = _PrefillParams(int(bool(causal)), float(softmax_scale), int(kv_tile), _RULES[p_rule],
+                       float(p_qmax), int(bool(l_from_quantized)))
+    dq, dk, dv = q.desc(), k.desc(), v.desc()
+    _check(_lib.mxattn_prefill(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(p),
+                               _ptr(out), _DT[out.dtype], _ptr(lse), _stream(q.codes)))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, hybrid=False):
+    return int(_lib.mxattn_decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, int(hybrid)))
+
+
+def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybrid=None,
+           q_bf16=None, workspace=None, return_lse=False, out=None):
+    """One query token per sequence against an MXFP4 KV cache.
+
+    q: MX [B,Hq,1,D]; caches: MX [B,Hkv,Tcap,D]; ctx_len int32 [B] on device.
+    hybrid: None or dict(idx, n_sel, k_sel, v_sel, k_win, v_win, window).
+    """
+    b, hq, _, d = q.shape
+    hkv, tcap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.codes.device
+    need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hybrid is not None)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((b, hq), dtype=torch.float32, device=dev) if return_lse else None
+    hy = None
+    if hybrid is not None:
+        hy = _Hybrid()
+        hy.idx, hy.n_sel = hybrid["idx"].data_ptr(), hybrid["n_sel"].data_ptr()
+        hy.max_sel = hybrid["idx"].shape[-1]
+        hy.window = int(hybrid["window"])
+        hy.k_sel, hy.v_sel = hybrid["k_sel"].data_ptr(), hybrid["v_sel"].data_ptr()
+        hy.k_win = hybrid["k_win"].data_ptr() if hybrid.get("k_win") is not None else None
+        hy.v_win = hybrid["v_win"].data_ptr() if hybrid.get("v_win") is not None else None
+    dq, dk, dv = q.desc(), k_cache.desc(), v_cache.desc()
+    _check(_lib.mxattn_decode(ctypes.byref(dq), _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv),
+                              _ptr(ctx_len), ctypes.byref(hy) if hy is not None else None,
+                              float(softmax_scale), int(split_len), _ptr(workspace), workspace.numel(),
+                              _ptr(out), _ptr(lse), _stream(q.codes)))
+    return (out, lse) if return_lse else out
+
+
+def select_workspace_bytes(batch, hq, recent, tcap):
+    return int(_lib.mxattn_select_workspace_bytes(batch, hq, recent, tcap))
+
+
+def select_vertical(q_recent, k_cache, ctx_len, col_mass, window, rho_num=5, rho_den=100,
+                    max_sel=None, softmax_scale=0.0, workspace=None):
+    """Accumulate column mass (in place) and select vertical-line tokens.
+
+    Returns (idx int32 [B,Hkv,max_sel] ascending, n int32 [B,Hkv])."""
+    b, hkv, tcap, d = k_cache.shape
+    dev = k_cache.codes.device
+    if max_sel is None:
+        max_sel = max(-(-(tcap - window) * rho_num // rho_den), 1)
+    hq = q_recent.shape[1] if q_recent is not None else hkv
+    r = q_recent.shape[2] if q_recent is not None else 0
+    need = select_workspace_bytes(b, hq, r, tcap)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    idx = torch.empty((b, hkv, max_sel), dtype=torch.int32, device=dev)
+    n = torch.empty((b, hkv), dtype=torch.int32, device=dev)
+    dq = q_recent.desc() if q_recent is not None else None
+    dk = k_cache.desc()
+    _check(_lib.mxattn_select_vertical(ctypes.byref(dq) if dq is not None else None, ctypes.byref(dk),
+                                       _ptr(ctx_len), float(softmax_scale), int(window), int(rho_num),
+                                       int(rho_den), _ptr(col_mass), _ptr(idx), _ptr(n), int(max_sel),
+                                       _ptr(workspace), workspace.numel(), _stream(k_cache.codes)))
+    return idx, n

@@ -1,0 +1,384 @@
+// Host side of libmxattn.so: argument validation, workspace sizing, kernel
+// dispatch, status strings.  Every check runs before any launch, so an error
+// status leaves all outputs untouched.
+//
+// Debug environment variables:
+//   MXATTN_SYNC=1               synchronise the stream after each launch and
+//                               report device errors as MXATTN_ERR_HIP.
+//   MXATTN_INJECT=<fn>:<code>   make entry point <fn> (e.g. "prefill") return
+//                               status <code> without launching (tests of the
+//                               callers' error handling).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/mxattn.h"
+#include "kernels.h"
+
+using namespace mxattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mxattn_status_t fail(mxattn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mxattn_status_t ok() {
+  g_last_error.clear();
+  return MXATTN_OK;
+}
+
+bool injected(const char* fn, mxattn_status_t* st) {
+  const char* env = getenv("MXATTN_INJECT");
+  if (env == nullptr) return false;
+  const char* colon = strchr(env, ':');
+  if (colon == nullptr) return false;
+  if (strncmp(env, fn, colon - env) != 0 || strlen(fn) != static_cast<size_t>(colon - env)) return false;
+  *st = static_cast<mxattn_status_t>(atoi(colon + 1));
+  g_last_error = std::string("injected failure in ") + fn;
+  return true;
+}
+
+mxattn_status_t after_launch(hipError_t e, hipStream_t stream, const char* what) {
+  if (e != hipSuccess) return fail(MXATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  const char* sync = getenv("MXATTN_SYNC");
+  if (sync != nullptr && sync[0] == '1') {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(MXATTN_ERR_HIP, "%s: device error: %s", what, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t key_blocks(int64_t s) { return (s + 31) / 32; }
+
+// Shape / stride / alignment checks of one MXFP4 descriptor.
+mxattn_status_t check_mx(const mxattn_mx_t* t, const char* name, int want_layout) {
+  if (t == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "%s: null descriptor", name);
+  if (t->codes == nullptr || t->scales == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "%s: null codes/scales", name);
+  if (t->layout != MXATTN_LAYOUT_HD && t->layout != MXATTN_LAYOUT_KEY)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: unknown layout %d", name, t->layout);
+  if (want_layout >= 0 && t->layout != want_layout)
+    return fail(MXATTN_ERR_UNSUPPORTED, "%s: layout must be %s", name, want_layout == 0 ? "HD" : "KEY");
+  if (t->batch < 1 || t->heads < 1 || t->seq < 1)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: empty shape [%lld,%lld,%lld,%lld]", name, (long long)t->batch,
+                (long long)t->heads, (long long)t->seq, (long long)t->dim);
+  if (t->dim != 64 && t->dim != 128) return fail(MXATTN_ERR_UNSUPPORTED, "%s: head_dim %lld not in {64,128}", name, (long long)t->dim);
+  if (!aligned16(t->codes)) return fail(MXATTN_ERR_INVALID_ARG, "%s: codes not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i)
+    if (t->code_stride[i] < 0 || t->code_stride[i] % 16 != 0 || t->scale_stride[i] < 0)
+      return fail(MXATTN_ERR_INVALID_ARG, "%s: code strides must be non-negative multiples of 16", name);
+  const int64_t row_codes = t->layout == MXATTN_LAYOUT_HD ? t->dim / 2 : key_blocks(t->seq) * 16;
+  const int64_t row_scales = t->layout == MXATTN_LAYOUT_HD ? t->dim / 32 : key_blocks(t->seq);
+  if (t->code_stride[2] < row_codes || t->scale_stride[2] < row_scales)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: row stride smaller than a row", name);
+  const int64_t rows = t->layout == MXATTN_LAYOUT_HD ? t->seq : t->dim;
+  if (t->code_stride[1] < rows * t->code_stride[2] && t->heads > 1)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: head stride overlaps rows", name);
+  if (t->code_stride[0] < t->heads * t->code_stride[1] && t->batch > 1 && t->code_stride[1] > 0)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: batch stride overlaps heads", name);
+  return MXATTN_OK;
+}
+
+MxView view_of(const mxattn_mx_t* t) {
+  MxView v;
+  v.codes = t->codes;
+  v.scales = t->scales;
+  for (int i = 0; i < 3; ++i) {
+    v.cs[i] = t->code_stride[i];
+    v.ss[i] = t->scale_stride[i];
+  }
+  return v;
+}
+
+bool valid_qmax(float q) { return q > 4.0f && q < 8.0f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxattn_version(void) { return "mxattn 0.1 (gfx950)"; }
+
+const char* mxattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* mxattn_status_string(mxattn_status_t s) {
+  switch (s) {
+    case MXATTN_OK: return "ok";
+    case MXATTN_ERR_INVALID_ARG: return "invalid argument";
+    case MXATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MXATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
+                                const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                const mxattn_mx_t* out, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("quantize", &st)) return st;
+  if (x == nullptr || x_stride == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "quantize: null input");
+  if (x_dtype != MXATTN_F32 && x_dtype != MXATTN_F16 && x_dtype != MXATTN_BF16)
+    return fail(MXATTN_ERR_INVALID_ARG, "quantize: unknown dtype %d", (int)x_dtype);
+  if (rule != MXATTN_SCALE_OCP && rule != MXATTN_SCALE_UOS) return fail(MXATTN_ERR_INVALID_ARG, "quantize: unknown rule");
+  if (rule == MXATTN_SCALE_UOS && !valid_qmax(qmax)) return fail(MXATTN_ERR_UNSUPPORTED, "quantize: UOS qmax must lie in (4, 8)");
+  if ((st = check_mx(out, "quantize.out", -1)) != MXATTN_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if (x_stride[i] < 0) return fail(MXATTN_ERR_INVALID_ARG, "quantize: negative input stride");
+  const int esz = x_dtype == MXATTN_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(x) % esz) != 0) return fail(MXATTN_ERR_INVALID_ARG, "quantize: misaligned input");
+  QuantArgs a{};
+  a.x = x;
+  a.dtype = x_dtype == MXATTN_F32 ? 0 : (x_dtype == MXATTN_F16 ? 1 : 2);
+  for (int i = 0; i < 3; ++i) {
+    a.xs[i] = x_stride[i];
+    a.cs[i] = out->code_stride[i];
+    a.ss[i] = out->scale_stride[i];
+  }
+  a.chan_scale = chan_scale;
+  a.uos = rule == MXATTN_SCALE_UOS;
+  a.qmax_quarter = qmax * 0.25f;
+  a.key_layout = out->layout == MXATTN_LAYOUT_KEY;
+  a.B = out->batch;
+  a.H = out->heads;
+  a.S = out->seq;
+  a.D = out->dim;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_quantize(a, s), s, "quantize");
+}
+
+mxattn_status_t mxattn_smooth_calibrate(const void* q_cal, const void* k_cal, mxattn_dtype_t dtype, int64_t hq,
+                                        int64_t hkv, int64_t tokens, int64_t dim, float* q_scale, float* k_scale,
+                                        mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("smooth_calibrate", &st)) return st;
+  if (!q_cal || !k_cal || !q_scale || !k_scale) return fail(MXATTN_ERR_INVALID_ARG, "smooth_calibrate: null pointer");
+  if (dtype != MXATTN_F32 && dtype != MXATTN_F16 && dtype != MXATTN_BF16)
+    return fail(MXATTN_ERR_INVALID_ARG, "smooth_calibrate: unknown dtype");
+  if (hq < 1 || hkv < 1 || tokens < 1 || dim < 1) return fail(MXATTN_ERR_INVALID_ARG, "smooth_calibrate: empty shape");
+  if (hq % hkv != 0) return fail(MXATTN_ERR_INVALID_ARG, "smooth_calibrate: Hq %% Hkv != 0");
+  if (dim > 256) return fail(MXATTN_ERR_UNSUPPORTED, "smooth_calibrate: dim > 256");
+  CalibArgs a{};
+  a.q = q_cal;
+  a.k = k_cal;
+  a.dtype = dtype == MXATTN_F32 ? 0 : (dtype == MXATTN_F16 ? 1 : 2);
+  a.hq = static_cast<int>(hq);
+  a.hkv = static_cast<int>(hkv);
+  a.tokens = tokens;
+  a.dim = static_cast<int>(dim);
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_smooth_calibrate(a, s), s, "smooth_calibrate");
+}
+
+mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
+                               const mxattn_prefill_params_t* p, void* out, mxattn_dtype_t out_dtype, float* lse,
+                               mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("prefill", &st)) return st;
+  if ((st = check_mx(q, "prefill.q", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if ((st = check_mx(k, "prefill.k", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if ((st = check_mx(v, "prefill.v", MXATTN_LAYOUT_KEY)) != MXATTN_OK) return st;
+  if (p == nullptr || out == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "prefill: null params/out");
+  if (q->dim != k->dim || k->dim != v->dim) return fail(MXATTN_ERR_INVALID_ARG, "prefill: head_dim mismatch");
+  if (q->batch != k->batch || k->batch != v->batch) return fail(MXATTN_ERR_INVALID_ARG, "prefill: batch mismatch");
+  if (k->heads != v->heads || k->seq != v->seq) return fail(MXATTN_ERR_INVALID_ARG, "prefill: K/V shape mismatch");
+  if (q->heads % k->heads != 0) return fail(MXATTN_ERR_INVALID_ARG, "prefill: Hq %% Hkv != 0");
+  if (p->causal && q->seq != k->seq) return fail(MXATTN_ERR_UNSUPPORTED, "prefill: causal needs Sq == Sk");
+  const int kv_tile = p->kv_tile == 0 ? 128 : p->kv_tile;
+  if (kv_tile != 64 && kv_tile != 128 && kv_tile != 256)
+    return fail(MXATTN_ERR_UNSUPPORTED, "prefill: kv_tile %d not in {64,128,256}", kv_tile);
+  if (p->p_rule != MXATTN_SCALE_OCP && p->p_rule != MXATTN_SCALE_UOS)
+    return fail(MXATTN_ERR_INVALID_ARG, "prefill: unknown p_rule");
+  if (p->p_rule == MXATTN_SCALE_UOS && !valid_qmax(p->p_qmax))
+    return fail(MXATTN_ERR_UNSUPPORTED, "prefill: UOS p_qmax must lie in (4, 8)");
+  if (out_dtype != MXATTN_F32 && out_dtype != MXATTN_F16 && out_dtype != MXATTN_BF16)
+    return fail(MXATTN_ERR_INVALID_ARG, "prefill: unknown out dtype");
+  if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale))
+    return fail(MXATTN_ERR_INVALID_ARG, "prefill: softmax_scale must be finite and >= 0");
+  if (!aligned16(out)) return fail(MXATTN_ERR_INVALID_ARG, "prefill: out not 16-byte aligned");
+  const int64_t grid = ((q->seq + 127) / 128) * q->batch * q->heads;
+  if (grid > 0x7FFFFFFF || q->seq > 0x7FFFFFFF || k->seq > 0x7FFFFFFF)
+    return fail(MXATTN_ERR_UNSUPPORTED, "prefill: problem too large for one launch");
+  PrefillArgs a{};
+  a.q = view_of(q);
+  a.k = view_of(k);
+  a.v = view_of(v);
+  a.out = out;
+  a.lse = lse;
+  a.out_dtype = out_dtype == MXATTN_F32 ? 0 : (out_dtype == MXATTN_F16 ? 1 : 2);
+  a.B = static_cast<int>(q->batch);
+  a.Hq = static_cast<int>(q->heads);
+  a.Hkv = static_cast<int>(k->heads);
+  a.Sq = static_cast<int>(q->seq);
+  a.Sk = static_cast<int>(k->seq);
+  const float sm = p->softmax_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(q->dim)) : p->softmax_scale;
+  a.softmax_scale = sm;
+  a.c = sm * 1.4426950408889634f;
+  a.p_uos = p->p_rule == MXATTN_SCALE_UOS;
+  a.p_qmax_quarter = p->p_qmax * 0.25f;
+  a.l_from_quantized = p->l_from_quantized != 0;
+  a.n_qblk = static_cast<int>((q->seq + 127) / 128);
+  a.one_scale = 127;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_prefill(a, static_cast<int>(q->dim), kv_tile, p->causal != 0, s), s, "prefill");
+}
+
+size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int64_t dim, int64_t tcap,
+                                     int32_t split_len, int32_t hybrid) {
+  if (batch < 1 || hq < 1 || hkv < 1 || dim < 1 || tcap < 1 || split_len < 1) return 0;
+  const int64_t n_split = (tcap + split_len - 1) / split_len + (hybrid ? 1 : 0);
+  size_t bytes = static_cast<size_t>(batch * hq * n_split * (dim + 2)) * sizeof(float);
+  bytes = (bytes + 255) / 256 * 256;
+  if (hybrid) bytes += static_cast<size_t>(batch * hkv * ((tcap + 31) / 32)) * sizeof(uint32_t);
+  return bytes;
+}
+
+mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mxattn_mx_t* kc,
+                              const mxattn_mx_t* vc, const int32_t* ctx_len, const mxattn_hybrid_t* hy,
+                              float softmax_scale, int32_t split_len, void* workspace, size_t workspace_bytes,
+                              float* out, float* lse, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("decode", &st)) return st;
+  if ((st = check_mx(q, "decode.q", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if ((st = check_mx(kc, "decode.k_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if ((st = check_mx(vc, "decode.v_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if (ctx_len == nullptr || out == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode: null ctx_len/out");
+  if (q->seq != 1) return fail(MXATTN_ERR_UNSUPPORTED, "decode: one query token per sequence");
+  if (q->dim != kc->dim || kc->dim != vc->dim) return fail(MXATTN_ERR_INVALID_ARG, "decode: head_dim mismatch");
+  if (q->batch != kc->batch || kc->batch != vc->batch) return fail(MXATTN_ERR_INVALID_ARG, "decode: batch mismatch");
+  if (kc->heads != vc->heads || kc->seq != vc->seq) return fail(MXATTN_ERR_INVALID_ARG, "decode: K/V cache shape mismatch");
+  if (q->heads % kc->heads != 0) return fail(MXATTN_ERR_INVALID_ARG, "decode: Hq %% Hkv != 0");
+  const int64_t g = q->heads / kc->heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return fail(MXATTN_ERR_UNSUPPORTED, "decode: group size %lld", (long long)g);
+  if (split_len < 64 || split_len % 64 != 0) return fail(MXATTN_ERR_UNSUPPORTED, "decode: split_len must be a positive multiple of 64");
+  if (!(softmax_scale >= 0.0f) || !std::isfinite(softmax_scale))
+    return fail(MXATTN_ERR_INVALID_ARG, "decode: softmax_scale must be finite and >= 0");
+  if (kc->seq > 0x7FFFFFFF) return fail(MXATTN_ERR_UNSUPPORTED, "decode: cache too long");
+  const int hybrid = hy != nullptr;
+  if (hybrid) {
+    if (q_bf16 == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid needs q_bf16");
+    if (hy->window < 0 || hy->max_sel < 0) return fail(MXATTN_ERR_INVALID_ARG, "decode: negative window/max_sel");
+    if (hy->max_sel > 0 && (!hy->idx || !hy->n_sel || !hy->k_sel || !hy->v_sel))
+      return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid selected set pointers missing");
+    if (hy->window > 0 && (!hy->k_win || !hy->v_win)) return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid window pointers missing");
+    if (hy->max_sel + static_cast<int64_t>(hy->window) > kc->seq)
+      return fail(MXATTN_ERR_INVALID_ARG, "decode: max_sel + window exceeds the cache");
+  }
+  const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, kc->seq, split_len, hybrid);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MXATTN_ERR_WORKSPACE, "decode: workspace of %zu bytes needed", need);
+  if (!aligned16(workspace)) return fail(MXATTN_ERR_INVALID_ARG, "decode: workspace not 16-byte aligned");
+  DecodeArgs a{};
+  a.q = view_of(q);
+  a.k = view_of(kc);
+  a.v = view_of(vc);
+  a.ctx_len = ctx_len;
+  a.B = static_cast<int>(q->batch);
+  a.Hq = static_cast<int>(q->heads);
+  a.Hkv = static_cast<int>(kc->heads);
+  a.Tcap = static_cast<int>(kc->seq);
+  const float sm = softmax_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(q->dim)) : softmax_scale;
+  a.softmax_scale = sm;
+  a.c = sm * 1.4426950408889634f;
+  a.split_len = split_len;
+  a.n_split = static_cast<int>((kc->seq + split_len - 1) / split_len);
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.lse = lse;
+  a.hybrid = hybrid;
+  if (hybrid) {
+    a.q_bf16 = static_cast<const uint16_t*>(q_bf16);
+    a.idx = hy->idx;
+    a.n_sel = hy->n_sel;
+    a.max_sel = hy->max_sel;
+    a.window = hy->window;
+    a.k_sel = static_cast<const uint16_t*>(hy->k_sel);
+    a.v_sel = static_cast<const uint16_t*>(hy->v_sel);
+    a.k_win = static_cast<const uint16_t*>(hy->k_win);
+    a.v_win = static_cast<const uint16_t*>(hy->v_win);
+    size_t part_bytes = static_cast<size_t>(a.B) * a.Hq * (a.n_split + 1) * (q->dim + 2) * sizeof(float);
+    part_bytes = (part_bytes + 255) / 256 * 256;
+    a.mask = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + part_bytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_decode(a, static_cast<int>(q->dim), s), s, "decode");
+}
+
+// Per (batch, query head, recent query, context chunk): partial (max, sum)
+// of the logits; chunk = kSelectChunk keys.
+static constexpr int64_t kSelectChunk = 2048;
+
+size_t mxattn_select_workspace_bytes(int64_t batch, int64_t hq, int64_t recent, int64_t tcap) {
+  if (batch < 1 || hq < 1 || recent < 0 || tcap < 1) return 0;
+  const int64_t nchunk = (tcap + kSelectChunk - 1) / kSelectChunk;
+  const int64_t n = batch * hq * (recent > 0 ? recent : 1) * (nchunk + 1) * 2;
+  return static_cast<size_t>(n) * sizeof(float);
+}
+
+mxattn_status_t mxattn_select_vertical(const mxattn_mx_t* q, const mxattn_mx_t* kc, const int32_t* ctx_len,
+                                       float softmax_scale, int32_t window, int32_t rho_num, int32_t rho_den,
+                                       float* col_mass, int32_t* idx_out, int32_t* n_out, int32_t max_sel,
+                                       void* workspace, size_t workspace_bytes, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("select_vertical", &st)) return st;
+  if ((st = check_mx(kc, "select.k_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if (q != nullptr && (st = check_mx(q, "select.q_recent", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if (!ctx_len || !col_mass || !idx_out || !n_out) return fail(MXATTN_ERR_INVALID_ARG, "select: null pointer");
+  if (window < 0 || rho_num < 0 || rho_den < 1 || rho_num > rho_den || max_sel < 0)
+    return fail(MXATTN_ERR_INVALID_ARG, "select: bad window / rho / max_sel");
+  const int R = q ? static_cast<int>(q->seq) : 0;
+  if (q) {
+    if (q->dim != kc->dim || q->batch != kc->batch) return fail(MXATTN_ERR_INVALID_ARG, "select: shape mismatch");
+    if (q->heads % kc->heads != 0) return fail(MXATTN_ERR_INVALID_ARG, "select: Hq %% Hkv != 0");
+    if (R > 64) return fail(MXATTN_ERR_UNSUPPORTED, "select: more than 64 recent queries");
+  }
+  if (kc->seq > 65536) return fail(MXATTN_ERR_UNSUPPORTED, "select: cache longer than 65536");
+  const int64_t worst = kc->seq > window ? ((kc->seq - window) * rho_num + rho_den - 1) / rho_den : 0;
+  if (worst > max_sel) return fail(MXATTN_ERR_INVALID_ARG, "select: max_sel %d below the worst-case count %lld", max_sel, (long long)worst);
+  const size_t need = mxattn_select_workspace_bytes(kc->batch, q ? q->heads : kc->heads, R, kc->seq);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MXATTN_ERR_WORKSPACE, "select: workspace of %zu bytes needed", need);
+  if (!aligned16(workspace)) return fail(MXATTN_ERR_INVALID_ARG, "select: workspace not 16-byte aligned");
+  SelectArgs a{};
+  a.stats = static_cast<float*>(workspace);
+  a.chunk = static_cast<int>(kSelectChunk);
+  if (q) a.q = view_of(q);
+  a.k = view_of(kc);
+  a.ctx_len = ctx_len;
+  a.B = static_cast<int>(kc->batch);
+  a.Hq = q ? static_cast<int>(q->heads) : static_cast<int>(kc->heads);
+  a.Hkv = static_cast<int>(kc->heads);
+  a.R = R;
+  a.Tcap = static_cast<int>(kc->seq);
+  const float sm = softmax_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kc->dim)) : softmax_scale;
+  a.c = sm * 1.4426950408889634f;
+  a.window = window;
+  a.rho_num = rho_num;
+  a.rho_den = rho_den;
+  a.max_sel = max_sel;
+  a.col_mass = col_mass;
+  a.idx_out = idx_out;
+  a.n_out = n_out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_select(a, static_cast<int>(kc->dim), s), s, "select_vertical");
+}
+
+}  // extern "C"

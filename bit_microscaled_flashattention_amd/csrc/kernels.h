@@ -1,0 +1,102 @@
+// Kernel argument blocks and launchers shared between the host dispatch
+// (api.cpp) and the device sources.  Plain structs passed by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxattn {
+
+struct QuantArgs {
+  const void* x;
+  int dtype;  // 0 f32, 1 f16, 2 bf16
+  int64_t xs[3];
+  const float* chan_scale;
+  int uos;
+  float qmax_quarter;
+  int key_layout;
+  int64_t B, H, S, D;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t cs[3];
+  int64_t ss[3];
+};
+
+struct CalibArgs {
+  const void* q;
+  const void* k;
+  int dtype;
+  int hq, hkv;
+  int64_t tokens;
+  int dim;
+  float* q_scale;
+  float* k_scale;
+};
+
+// One MXFP4 operand as the kernels see it: base pointers and byte strides of
+// the (batch, head, row) dimensions.
+struct MxView {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t cs[3];
+  int64_t ss[3];
+};
+
+struct PrefillArgs {
+  MxView q, k, v;
+  void* out;
+  float* lse;
+  int out_dtype;
+  int B, Hq, Hkv, Sq, Sk;
+  float c;              // softmax_scale * log2(e)
+  float softmax_scale;
+  int p_uos;
+  float p_qmax_quarter;
+  int l_from_quantized;
+  int n_qblk;           // query blocks of 128 rows
+  int one_scale;        // 127, kept in a kernel argument so it stays a register value
+};
+
+struct DecodeArgs {
+  MxView q, k, v;
+  const int32_t* ctx_len;
+  int B, Hq, Hkv, Tcap;
+  float c;
+  float softmax_scale;
+  int split_len, n_split;
+  float* part;          // [B][Hq][n_split+1][D+2] partial (O, m, l)
+  float* out;
+  float* lse;
+  // hybrid
+  int hybrid;
+  const uint16_t* q_bf16;
+  const int32_t* idx;
+  const int32_t* n_sel;
+  int max_sel, window;
+  const uint16_t* k_sel;
+  const uint16_t* v_sel;
+  const uint16_t* k_win;
+  const uint16_t* v_win;
+  uint32_t* mask;       // [B][Hkv][Tcap/32] bitmap of bf16-held tokens
+};
+
+struct SelectArgs {
+  MxView q, k;
+  const int32_t* ctx_len;
+  int B, Hq, Hkv, R, Tcap;
+  float c;
+  int window, rho_num, rho_den, max_sel;
+  float* col_mass;
+  float* stats;         // [B][Hq][R][nchunk+1][2] partial row max / sum (workspace)
+  int chunk;            // keys per context chunk
+  int32_t* idx_out;
+  int32_t* n_out;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_smooth_calibrate(const CalibArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream);
+
+}  // namespace mxattn

@@ -1,0 +1,77 @@
+// Device-side helpers shared by the mxattn kernels (gfx950 only).
+//
+// MXFP4: blocks of 32 elements share one E8M0 scale; elements are FP4 E2M1
+// (BitDecoding-FP4 page, "The KV Cache Bottleneck in Long-Context LLM
+// Serving").  OCP and UOS scale rules: see include/mxattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxattn {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Value of element i of a row of bf16/fp16/fp32 data, widened to fp32.
+__device__ __forceinline__ float load_elem(const void* base, int64_t i, int dtype) {
+  if (dtype == 0) return reinterpret_cast<const float*>(base)[i];
+  uint16_t u = reinterpret_cast<const uint16_t*>(base)[i];
+  if (dtype == 2) return __uint_as_float(static_cast<uint32_t>(u) << 16);
+  return static_cast<float>(__builtin_bit_cast(_Float16, u));
+}
+
+// E8M0 byte for a block maximum given as the fp32 bit pattern of |amax|.
+// OCP: e = floor(log2 amax) - 2.  UOS: one more when amax / 2^e_ocp > qmax,
+// i.e. when the significand 1.m exceeds qmax/4 (qmax in (4, 8)).  Zero and
+// subnormal maxima land in the clamp region: byte 0 (e = -127).
+__device__ __forceinline__ int e8m0_byte(uint32_t amax_bits, bool uos, float qmax_quarter) {
+  int biased = static_cast<int>(amax_bits >> 23);
+  if (biased == 0) return 0;
+  int inc = 0;
+  if (uos) {
+    float sig = __uint_as_float(0x3F800000u | (amax_bits & 0x7FFFFFu));
+    inc = sig > qmax_quarter ? 1 : 0;
+  }
+  int b = biased - 2 + inc;
+  return b < 0 ? 0 : (b > 254 ? 254 : b);
+}
+
+// E2M1 code of fp32 value y in a block with scale byte sb, round to nearest
+// even with saturation; the sign bit is kept for values that round to 0.
+// |y| / 2^e is formed exactly with ldexp (denormals preserved) and placed
+// against the grid midpoints; a midpoint goes to its even neighbour.
+__device__ __forceinline__ uint32_t e2m1_code(float y, int sb) {
+  uint32_t sign = (__float_as_uint(y) >> 31) << 3;
+  float z = __builtin_ldexpf(__builtin_fabsf(y), 127 - sb);
+  uint32_t c = (z > 0.25f) + (z >= 0.75f) + (z > 1.25f) + (z >= 1.75f) + (z > 2.5f) +
+               (z >= 3.5f) + (z > 5.0f);
+  return c | sign;
+}
+
+// Scaled FP4 x FP4 MFMAs (E2M1 both sides, one E8M0 scale per lane held in
+// byte 0 of the scale operand).
+__device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f c, int sa, int sb) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ v4f mfma16_fp4(v4i a, v4i b, v4f c, int sa, int sb) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+
+// Hardware exp2 (v_exp_f32); results below 2^-126 flush to 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^(byte-127) as an fp32 scale for the convert instructions (byte >= 1).
+__device__ __forceinline__ float scale_of_byte(int b) { return __uint_as_float(static_cast<uint32_t>(b) << 23); }
+
+}  // namespace mxattn

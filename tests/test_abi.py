@@ -1,0 +1,180 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol include/mxattn.h declares, and rejects bad arguments with a status and
+a message before any launch; the fault-injection hook works."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_microscaled_flashattention_amd as mxa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mxattn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxattn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 9
+    lib = mxa.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mxa.EXPORTS) == names
+
+
+def test_status_strings_and_version():
+    lib = mxa.library()
+    for code, word in ((0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")):
+        assert word in lib.mxattn_status_string(code)
+    assert b"gfx950" in lib.mxattn_version()
+
+
+def _mx(codes=16, scales=16, b=1, h=1, s=128, d=128, layout=0):
+    m = mxa._Mx()
+    m.codes, m.scales = codes, scales
+    m.batch, m.heads, m.seq, m.dim = b, h, s, d
+    m.layout = layout
+    if layout == 0:
+        rc, rs = d // 2, d // 32
+        m.code_stride[:] = [h * s * rc, s * rc, rc]
+        m.scale_stride[:] = [h * s * rs, s * rs, rs]
+    else:
+        nb = (s + 31) // 32
+        m.code_stride[:] = [h * d * nb * 16, d * nb * 16, nb * 16]
+        m.scale_stride[:] = [h * d * nb, d * nb, nb]
+    return m
+
+
+def _prefill(q, k, v, **kw):
+    lib = mxa.library()
+    p = mxa._PrefillParams(kw.get("causal", 0), kw.get("scale", 0.0), kw.get("kv_tile", 128),
+                           kw.get("p_rule", 0), kw.get("p_qmax", 7.25), 1)
+    return lib.mxattn_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(p),
+                              ctypes.c_void_p(kw.get("out", 4096)), 0, None, None)
+
+
+@pytest.mark.parametrize("case, status", [
+    ("d96", mxa.ERR_UNSUPPORTED),
+    ("null_codes", mxa.ERR_INVALID_ARG),
+    ("misaligned_codes", mxa.ERR_INVALID_ARG),
+    ("v_not_key_layout", mxa.ERR_UNSUPPORTED),
+    ("gqa_mismatch", mxa.ERR_INVALID_ARG),
+    ("causal_rect", mxa.ERR_UNSUPPORTED),
+    ("kv_tile_96", mxa.ERR_UNSUPPORTED),
+    ("uos_qmax_9", mxa.ERR_UNSUPPORTED),
+    ("neg_scale", mxa.ERR_INVALID_ARG),
+    ("out_misaligned", mxa.ERR_INVALID_ARG),
+    ("short_row_stride", mxa.ERR_INVALID_ARG),
+])
+def test_prefill_rejects(case, status):
+    q, k, v = _mx(), _mx(), _mx(layout=1)
+    kw = {}
+    if case == "d96":
+        q, k, v = _mx(d=96), _mx(d=96), _mx(d=96, layout=1)
+    elif case == "null_codes":
+        q.codes = None
+    elif case == "misaligned_codes":
+        k.codes = 24
+    elif case == "v_not_key_layout":
+        v = _mx()
+    elif case == "gqa_mismatch":
+        q = _mx(h=3); k = _mx(h=2); v = _mx(h=2, layout=1)
+    elif case == "causal_rect":
+        q = _mx(s=64); kw["causal"] = 1
+    elif case == "kv_tile_96":
+        kw["kv_tile"] = 96
+    elif case == "uos_qmax_9":
+        kw["p_rule"], kw["p_qmax"] = 1, 9.0
+    elif case == "neg_scale":
+        kw["scale"] = -1.0
+    elif case == "out_misaligned":
+        kw["out"] = 4100
+    elif case == "short_row_stride":
+        k.code_stride[2] = 32
+    st = _prefill(q, k, v, **kw)
+    assert st == status
+    assert len(mxa.library().mxattn_last_error()) > 0
+
+
+def test_quantize_rejects_without_launch():
+    lib = mxa.library()
+    out = _mx()
+    strides = (ctypes.c_int64 * 3)(0, 0, 128)
+    assert lib.mxattn_quantize(None, 2, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize(ctypes.c_void_p(64), 7, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize(ctypes.c_void_p(64), 2, strides, None, 1, 8.5, ctypes.byref(out), None) == mxa.ERR_UNSUPPORTED
+    assert lib.mxattn_quantize(ctypes.c_void_p(65), 2, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+
+
+def test_calibrate_rejects():
+    lib = mxa.library()
+    f = ctypes.c_void_p(64)
+    assert lib.mxattn_smooth_calibrate(f, f, 2, 6, 4, 16, 128, f, f, None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_smooth_calibrate(f, f, 2, 8, 4, 16, 512, f, f, None) == mxa.ERR_UNSUPPORTED
+    assert lib.mxattn_smooth_calibrate(None, f, 2, 8, 4, 16, 128, f, f, None) == mxa.ERR_INVALID_ARG
+
+
+def test_decode_workspace_and_rejects():
+    lib = mxa.library()
+    n = mxa.decode_workspace_bytes(32, 32, 8, 128, 32768, 2048)
+    assert n == 32 * 32 * 16 * 130 * 4
+    nh = mxa.decode_workspace_bytes(8, 32, 8, 128, 32768, 2048, hybrid=True)
+    assert nh >= 8 * 32 * 17 * 130 * 4 + 8 * 8 * 1024 * 4
+    q = _mx(s=1, h=32); kc = _mx(s=32768, h=8); vc = _mx(s=32768, h=8)
+    ctx = ctypes.c_void_p(64)
+    out = ctypes.c_void_p(4096)
+    # workspace too small
+    st = lib.mxattn_decode(ctypes.byref(q), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 2048,
+                           ctypes.c_void_p(4096), 16, out, None, None)
+    assert st == mxa.ERR_WORKSPACE
+    # split_len not a multiple of 64
+    st = lib.mxattn_decode(ctypes.byref(q), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 100,
+                           ctypes.c_void_p(4096), 1 << 30, out, None, None)
+    assert st == mxa.ERR_UNSUPPORTED
+    # group of 3 query heads per KV head
+    q3 = _mx(s=1, h=24)
+    st = lib.mxattn_decode(ctypes.byref(q3), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 2048,
+                           ctypes.c_void_p(4096), 1 << 30, out, None, None)
+    assert st == mxa.ERR_UNSUPPORTED
+    # hybrid without a bf16 query
+    hy = mxa._Hybrid()
+    hy.max_sel, hy.window = 16, 8
+    st = lib.mxattn_decode(ctypes.byref(q), None, ctypes.byref(kc), ctypes.byref(vc), ctx, ctypes.byref(hy),
+                           0.0, 2048, ctypes.c_void_p(4096), 1 << 30, out, None, None)
+    assert st == mxa.ERR_INVALID_ARG
+
+
+def test_select_rejects():
+    lib = mxa.library()
+    kc = _mx(s=32768, h=8)
+    q = _mx(s=65, h=32)
+    f = ctypes.c_void_p(4096)
+    args = lambda qq, max_sel, ws: (ctypes.byref(qq) if qq else None, ctypes.byref(kc), f, 0.0, 128, 5, 100,
+                                    f, f, f, max_sel, f, ws, None)
+    assert lib.mxattn_select_vertical(*args(q, 4096, 1 << 30)) == mxa.ERR_UNSUPPORTED    # R > 64
+    q = _mx(s=64, h=32)
+    assert lib.mxattn_select_vertical(*args(q, 100, 1 << 30)) == mxa.ERR_INVALID_ARG     # max_sel too small
+    assert lib.mxattn_select_vertical(*args(q, 1632, 8)) == mxa.ERR_WORKSPACE
+
+
+def test_fault_injection(monkeypatch):
+    q, k, v = _mx(), _mx(), _mx(layout=1)
+    monkeypatch.setenv("MXATTN_INJECT", "prefill:4")
+    assert _prefill(q, k, v) == mxa.ERR_HIP
+    assert b"injected" in mxa.library().mxattn_last_error()
+    monkeypatch.setenv("MXATTN_INJECT", "decode:3")
+    # A different entry point is unaffected (and fails its own validation).
+    q.codes = None
+    assert _prefill(q, k, v) == mxa.ERR_INVALID_ARG
+
+
+def test_python_errors_raise():
+    with pytest.raises(mxa.MxattnError) as ei:
+        mxa._check(mxa.ERR_UNSUPPORTED)
+    assert ei.value.status == mxa.ERR_UNSUPPORTED

@@ -1,0 +1,168 @@
+"""GPU parity of the MXFP4 prefill against the float64 oracle on the same
+quantised operands: max |gpu - oracle| <= 2e-3 per row, plus the oracle's
+per-row float32 rounding envelope (rows whose P elements sit within float32
+reach of an E2M1 midpoint or scale boundary, where both codes are correct)."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_microscaled_flashattention_amd as mxa
+import synth
+from oracle import attention, mx, smooth
+from tests.helpers import (assert_codes_equal, check_within, head_slice, host_f64,
+                           oracle_dequant, oracle_quantize)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ATOL = 2e-3
+
+
+def _run_case(q, k, v, *, causal, kv_tile=128, p_rule="ocp", qkv_rule="ocp", l_from_quantized=True,
+              rows=None, q_scale=None, k_scale=None, out_dtype=torch.float32, heads=None, what=""):
+    """Quantise on the GPU, run prefill on every head, then check codes and
+    outputs against the oracle on ``heads`` (query heads, default all) and
+    ``rows`` (dict hq -> row indices, default all rows)."""
+    print(f"prefill case {what}: q{tuple(q.shape)} k{tuple(k.shape)} causal={causal} "
+          f"tile={kv_tile} p={p_rule}", flush=True)
+    qh = mxa.quantize(q, "hd", chan_scale=q_scale, rule=qkv_rule)
+    kh = mxa.quantize(k, "hd", chan_scale=k_scale, rule=qkv_rule)
+    vh = mxa.quantize(v, "key", rule=qkv_rule)
+    out, lse = mxa.prefill(qh, kh, vh, causal=causal, kv_tile=kv_tile, p_rule=p_rule,
+                           l_from_quantized=l_from_quantized, out_dtype=out_dtype, return_lse=True)
+    torch.cuda.synchronize()
+    bsz, hq, _, _ = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    heads = list(range(hq)) if heads is None else list(heads)
+    kv_heads = sorted({h // grp for h in heads})
+    r = mx.RULE_OCP if qkv_rule == "ocp" else mx.RULE_UOS
+    pr = mx.RULE_OCP if p_rule == "ocp" else mx.RULE_UOS
+    qsel = torch.as_tensor(heads, device=q.device)
+    ksel = torch.as_tensor(kv_heads, device=q.device)
+    q32 = host_f64(q.index_select(1, qsel)).astype(np.float32)
+    k32 = host_f64(k.index_select(1, ksel)).astype(np.float32)
+    if q_scale is not None:
+        q32 = smooth.apply(q32, q_scale.cpu().numpy()[heads])
+        k32 = smooth.apply(k32, k_scale.cpu().numpy()[kv_heads])
+    oq = oracle_quantize(q32.astype(np.float64), "hd", r)
+    ok = oracle_quantize(k32.astype(np.float64), "hd", r)
+    ov = oracle_quantize(host_f64(v.index_select(1, ksel)), "key", r)
+    assert_codes_equal(head_slice(qh, heads), *oq, what + " q")
+    assert_codes_equal(head_slice(kh, kv_heads), *ok, what + " k")
+    assert_codes_equal(head_slice(vh, kv_heads), *ov, what + " v")
+    qd = oracle_dequant(*oq, "hd")
+    kd = oracle_dequant(*ok, "hd")
+    vd = oracle_dequant(*ov, "key", n=v.shape[2])
+    got = out.float().cpu().numpy()
+    glse = lse.cpu().numpy()
+    atol = ATOL if out_dtype == torch.float32 else ATOL + 8e-3
+    worst, n_env = 0.0, 0
+    for bi in range(bsz):
+        for i, h in enumerate(heads):
+            kvi = kv_heads.index(h // grp)
+            rr = None if rows is None else rows[h]
+            res = attention.prefill_head(qd[bi, i], kd[bi, kvi], vd[bi, kvi], causal=causal,
+                                         kv_tile=kv_tile, p_rule=pr, l_from_quantized=l_from_quantized,
+                                         rows=rr, envelope=True)
+            g_rows = got[bi, h] if rr is None else got[bi, h][rr]
+            l_rows = glse[bi, h] if rr is None else glse[bi, h][rr]
+            worst = max(worst, check_within(g_rows, res["out"], res["bound"], atol, f"{what} b{bi} h{h}"))
+            n_env += int((res["bound"] > 0).sum())
+            np.testing.assert_allclose(l_rows, res["lse"], atol=1e-3, rtol=0)
+    print(f"  worst |err| {worst:.3e}; rows needing the envelope: {n_env}", flush=True)
+    return worst
+
+
+def test_tiny_workload_1():
+    """Batch 1, 1 head, S=128, D=64, fp16, non-causal, single key tile."""
+    d = synth.tiny(device=DEV)
+    _run_case(d["q"], d["k"], d["v"], causal=False, what="workload-1")
+
+
+@pytest.mark.parametrize("kv_tile", [64, 128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gqa_ragged_tiles(kv_tile, causal):
+    g = torch.Generator(device=DEV).manual_seed(21)
+    s = 333
+    q = torch.randn((1, 4, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((1, 2, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 2, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    _run_case(q, k, v, causal=causal, kv_tile=kv_tile, what=f"gqa ragged tile={kv_tile}")
+
+
+def test_rectangular_non_causal_d64_batch2():
+    g = torch.Generator(device=DEV).manual_seed(22)
+    q = torch.randn((2, 2, 200, 64), generator=g, device=DEV).to(torch.float16)
+    k = torch.randn((2, 1, 417, 64), generator=g, device=DEV).to(torch.float16)
+    v = torch.randn((2, 1, 417, 64), generator=g, device=DEV).to(torch.float16)
+    _run_case(q, k, v, causal=False, what="rect d64")
+
+
+@pytest.mark.parametrize("rule", ["uos", "ocp"])
+def test_uos_everywhere_and_baseline_normaliser(rule):
+    g = torch.Generator(device=DEV).manual_seed(23)
+    q = (torch.randn((1, 2, 260, 128), generator=g, device=DEV) * 2).to(torch.bfloat16)
+    k = torch.randn((1, 2, 260, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 2, 260, 128), generator=g, device=DEV).to(torch.bfloat16)
+    _run_case(q, k, v, causal=True, p_rule=rule, qkv_rule=rule, what=f"{rule} all")
+    _run_case(q, k, v, causal=True, p_rule=rule, l_from_quantized=False, what=f"{rule} baseline-l")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_low_precision_output(out_dtype):
+    g = torch.Generator(device=DEV).manual_seed(24)
+    q = torch.randn((1, 2, 130, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((1, 2, 130, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 2, 130, 128), generator=g, device=DEV).to(torch.bfloat16)
+    _run_case(q, k, v, causal=True, out_dtype=out_dtype, what=f"out {out_dtype}")
+
+
+def test_single_token_and_short():
+    g = torch.Generator(device=DEV).manual_seed(25)
+    for s in (1, 31, 33):
+        q = torch.randn((1, 1, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+        k = torch.randn((1, 1, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+        v = torch.randn((1, 1, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+        _run_case(q, k, v, causal=True, what=f"s={s}")
+
+
+def _sample_rows(seq, n, seed, heads):
+    """Rows 0, 1, 2, seq-1 and n distinct others, per head."""
+    rng = np.random.default_rng(seed)
+    return {h: np.sort(np.concatenate([[0, 1, 2, seq - 1], rng.choice(np.arange(3, seq - 1), size=n,
+                                                                       replace=False)]))
+            for h in heads}
+
+
+def test_workload_2_full_size_sampled_rows():
+    """Causal GQA 32/8 heads, S=4096, D=128, outlier K channels, static
+    Smooth-QK from the calibration slice; all codes compared, 24 sampled rows
+    per head compared with the oracle."""
+    d = synth.gqa_prefill(device=DEV)
+    qs, ks = mxa.smooth_calibrate(d["q_cal"], d["k_cal"])
+    rows = _sample_rows(4096, 20, 5, range(32))
+    _run_case(d["q"], d["k"], d["v"], causal=True, rows=rows, q_scale=qs, k_scale=ks,
+              what="workload-2 full")
+
+
+def test_workload_5_sampled_rows():
+    """Non-causal, 24 heads, S=32768, UOS on Q, K, V and P: all heads run,
+    three heads and ten rows each are compared with the oracle."""
+    d = synth.diffusion(device=DEV)
+    heads = [0, 7, 23]
+    rows = _sample_rows(32768, 6, 6, heads)
+    _run_case(d["q"], d["k"], d["v"], causal=False, p_rule="uos", qkv_rule="uos", rows=rows,
+              heads=heads, what="workload-5 full")
+
+
+def test_deterministic_and_launch_order_independent():
+    g = torch.Generator(device=DEV).manual_seed(26)
+    q = torch.randn((1, 8, 512, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((1, 2, 512, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 2, 512, 128), generator=g, device=DEV).to(torch.bfloat16)
+    qh, kh, vh = mxa.quantize(q), mxa.quantize(k), mxa.quantize(v, "key")
+    a = mxa.prefill(qh, kh, vh, causal=True)
+    b = mxa.prefill(qh, kh, vh, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

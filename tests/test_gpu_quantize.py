@@ -1,0 +1,134 @@
+"""GPU parity of the MXFP4 quantiser and the Smooth-QK calibration against the
+oracle: codes, scale bytes and calibration factors must match bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_microscaled_flashattention_amd as mxa
+import synth
+from oracle import mx, smooth
+from tests.helpers import assert_codes_equal, host_f64, oracle_quantize
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _all_bf16_blocks(n_perm=4, seed=0):
+    """Every finite bf16 pattern, shuffled into 32-element blocks n_perm
+    times (each pattern meets several different block maxima)."""
+    bits = np.arange(65536, dtype=np.uint32)
+    exp = (bits >> 7) & 0xFF
+    bits = bits[exp != 0xFF].astype(np.uint16)          # drop Inf/NaN
+    rng = np.random.default_rng(seed)
+    rows = []
+    for _ in range(n_perm):
+        p = rng.permutation(bits)
+        p = p[: (p.shape[0] // 128) * 128]
+        rows.append(p.reshape(-1, 128))
+    arr = np.concatenate(rows)                           # [S, 128]
+    t = torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16)
+    return t.reshape(1, 1, -1, 128)
+
+
+def _tiny_magnitude_blocks(seed=1):
+    """Blocks whose maxima sit in and around the subnormal / clamp range and
+    near every power of two and UOS boundary."""
+    rng = np.random.default_rng(seed)
+    vals = []
+    for e in list(range(-149, -110)) + list(range(-5, 6)) + [100, 126, 127]:
+        base = np.ldexp(rng.uniform(-1, 1, size=(4, 128)), e)
+        base[:, 0] = np.ldexp(7.25, e - 2) * np.array([1, 1 + 2 ** -10, 1 - 2 ** -10, 1])
+        base[:, 33] = np.ldexp(1.0, e) * np.array([1, 1 + 2 ** -7, 1 - 2 ** -7, -1])
+        vals.append(base)
+    x = np.concatenate(vals).astype(np.float32)
+    return torch.from_numpy(x).reshape(1, 1, -1, 128)
+
+
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+@pytest.mark.parametrize("layout", ["hd", "key"])
+def test_quantize_all_bf16_patterns(rule, layout):
+    x = _all_bf16_blocks()
+    print(f"quantize all-bf16 rule={rule} layout={layout} shape={tuple(x.shape)}", flush=True)
+    got = mxa.quantize(x.to(DEV), layout=layout, rule=rule)
+    torch.cuda.synchronize()
+    r = mx.RULE_OCP if rule == "ocp" else mx.RULE_UOS
+    oc, os_ = oracle_quantize(host_f64(x), layout, r)
+    assert_codes_equal(got, oc, os_, f"bf16 patterns {rule}/{layout}")
+
+
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_quantize_fp32_subnormal_and_boundaries(rule):
+    x = _tiny_magnitude_blocks()
+    got = mxa.quantize(x.to(DEV), layout="hd", rule=rule)
+    torch.cuda.synchronize()
+    r = mx.RULE_OCP if rule == "ocp" else mx.RULE_UOS
+    oc, os_ = oracle_quantize(host_f64(x), "hd", r)
+    assert_codes_equal(got, oc, os_, "fp32 boundary blocks")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("layout", ["hd", "key"])
+def test_quantize_with_channel_scale_and_ragged_seq(dtype, layout):
+    g = torch.Generator().manual_seed(11)
+    x = (torch.randn((2, 3, 77, 64), generator=g) * 3).to(dtype)
+    cs = torch.exp(torch.randn((3, 64), generator=g)).to(torch.float32)
+    got = mxa.quantize(x.to(DEV), layout=layout, chan_scale=cs.to(DEV))
+    torch.cuda.synchronize()
+    x32 = smooth.apply(host_f64(x).astype(np.float32).reshape(2, 3, 77, 64), cs.numpy())
+    oc, os_ = oracle_quantize(x32.astype(np.float64), layout)
+    assert_codes_equal(got, oc, os_, f"{dtype}/{layout}")
+    if layout == "key":
+        gc = mx.unpack_nibbles(got.codes.cpu().numpy(), axis=-1)
+        assert (gc[..., 77:] == 0).all(), "padding past the sequence must be code 0"
+
+
+def test_quantize_strided_input_into_cache_rows():
+    """Writing one token into row t of a larger cache (decode append) through
+    the stride arguments."""
+    g = torch.Generator().manual_seed(12)
+    cache = mxa.empty_mx((2, 4, 40, 128), "hd", DEV)
+    cache.codes.zero_(); cache.scales.zero_()
+    x = torch.randn((2, 4, 1, 128), generator=g).to(torch.bfloat16).to(DEV)
+    row = cache.narrow_seq(17, 1)
+    mxa.quantize(x, layout="hd", out=row)
+    torch.cuda.synchronize()
+    oc, os_ = oracle_quantize(host_f64(x), "hd")
+    full_c = mx.unpack_nibbles(cache.codes.cpu().numpy(), axis=-1)
+    np.testing.assert_array_equal(full_c[:, :, 17], oc[:, :, 0])
+    np.testing.assert_array_equal(cache.scales.cpu().numpy()[:, :, 17], os_[:, :, 0])
+    assert (full_c[:, :, :17] == 0).all() and (full_c[:, :, 18:] == 0).all()
+
+
+def test_workload_shapes_q_k_v():
+    d = synth.gqa_prefill(device=DEV, seq=512)
+    for name, layout in (("q", "hd"), ("k", "hd"), ("v", "key")):
+        got = mxa.quantize(d[name], layout=layout)
+        torch.cuda.synchronize()
+        oc, os_ = oracle_quantize(host_f64(d[name]), layout)
+        assert_codes_equal(got, oc, os_, f"workload-2 {name}")
+
+
+def test_smooth_calibration_bit_exact():
+    d = synth.gqa_prefill(device=DEV, seq=128)
+    qs, ks = mxa.smooth_calibrate(d["q_cal"], d["k_cal"])
+    torch.cuda.synchronize()
+    oq, ok = smooth.calibrate(host_f64(d["q_cal"]), host_f64(d["k_cal"]))
+    np.testing.assert_array_equal(qs.cpu().numpy(), oq)
+    np.testing.assert_array_equal(ks.cpu().numpy(), ok)
+    # The outlier channels get factors well above 1 (difficulty moves to Q).
+    ch = d["outlier_channels"].numpy()
+    for h in range(ch.shape[0]):
+        assert (oq[4 * h, ch[h]] > 2.0).all()
+
+
+def test_smooth_calibration_special_values():
+    q = torch.zeros((4, 8, 64)); k = torch.zeros((2, 8, 64))
+    q[0, 3, 1] = 1.0; k[0, 2, 1] = 2.0 ** 30             # clamp at 2^8
+    q[1, 0, 2] = 3.0                                      # k max 0 -> 1
+    k[1, 5, 3] = 5.0; q[2, 1, 3] = -0.75                  # ordinary ratio
+    qs, ks = mxa.smooth_calibrate(q.to(torch.bfloat16).to(DEV), k.to(torch.bfloat16).to(DEV))
+    torch.cuda.synchronize()
+    oq, ok = smooth.calibrate(q.numpy(), k.numpy())
+    np.testing.assert_array_equal(qs.cpu().numpy(), oq)
+    np.testing.assert_array_equal(ks.cpu().numpy(), ok)
