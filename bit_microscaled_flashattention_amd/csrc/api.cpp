@@ -279,6 +279,7 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
     if (hy->max_sel > 0 && (!hy->idx || !hy->n_sel || !hy->k_sel || !hy->v_sel))
       return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid selected set pointers missing");
     if (hy->window > 0 && (!hy->k_win || !hy->v_win)) return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid window pointers missing");
+    if (kc->seq > (1 << 19)) return fail(MXATTN_ERR_UNSUPPORTED, "decode: hybrid needs Tcap <= 524288");
     if (hy->max_sel + static_cast<int64_t>(hy->window) > kc->seq)
       return fail(MXATTN_ERR_INVALID_ARG, "decode: max_sel + window exceeds the cache");
   }
@@ -349,6 +350,8 @@ mxattn_status_t mxattn_select_vertical(const mxattn_mx_t* q, const mxattn_mx_t* 
     if (q->dim != kc->dim || q->batch != kc->batch) return fail(MXATTN_ERR_INVALID_ARG, "select: shape mismatch");
     if (q->heads % kc->heads != 0) return fail(MXATTN_ERR_INVALID_ARG, "select: Hq %% Hkv != 0");
     if (R > 64) return fail(MXATTN_ERR_UNSUPPORTED, "select: more than 64 recent queries");
+    if ((q->heads / kc->heads) * R > 512)
+      return fail(MXATTN_ERR_UNSUPPORTED, "select: recent queries x group size above 512");
   }
   if (kc->seq > 65536) return fail(MXATTN_ERR_UNSUPPORTED, "select: cache longer than 65536");
   const int64_t worst = kc->seq > window ? ((kc->seq - window) * rho_num + rho_den - 1) / rho_den : 0;

@@ -88,8 +88,11 @@ def long_decode(device="cpu", batch=32, hq=32, hkv=8, ctx=32768, head_dim=128, w
 
 
 # ---------------------------------------------------------------- workload 4
-HYBRID_GAMMA = 0.5     # key offset gain along the bias direction
-HYBRID_BETA = 6.0      # query offset along the bias direction
+# Chosen so that the heaviest 5% of the non-window keys carry about 60% of the
+# attention mass of the recent queries (mean over the KV heads; the HyQuant
+# page reports 54-64% for real models).  Checked by tests/test_synth.py.
+HYBRID_GAMMA = 0.19    # key offset gain along the bias direction
+HYBRID_BETA = 1.0      # query offset along the bias direction
 PARETO_SHAPE = 1.5
 
 

@@ -1,0 +1,263 @@
+"""GPU parity of MXFP4 decode (plain and hybrid) and of vertical-line
+selection against the oracle.  Decode outputs must match within 2e-3 max-abs
+(P is not quantised, so no rounding envelope is involved); cache codes are
+compared bit for bit; the top-k is compared exactly where the masses are
+exact and, for float masses, on what is unique (indices clearly above or
+below the threshold) with the rest checked for validity."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_microscaled_flashattention_amd as mxa
+import synth
+from oracle import attention, mx, select
+from tests.helpers import assert_codes_equal, head_slice, host_f64, oracle_dequant, oracle_quantize
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ATOL = 2e-3
+
+
+def _cache(k, v):
+    return mxa.quantize(k, "hd"), mxa.quantize(v, "hd")
+
+
+def _query(q):
+    return mxa.quantize(q[:, :, None, :], "hd")
+
+
+def _oracle_pair(q, k, v, ctx, pairs, hybrid_sets=None, q_bf=None):
+    """Oracle decode on (b, hq) pairs from the generator tensors."""
+    hq, hkv = q.shape[1], k.shape[1]
+    g = hq // hkv
+    res = {}
+    qd_all = oracle_dequant(*oracle_quantize(host_f64(q[:, :, None, :]), "hd"), "hd")[:, :, 0]
+    cache = {}
+    for (b, h) in pairs:
+        kv = h // g
+        if (b, kv) not in cache:
+            kk = host_f64(k[b:b + 1, kv:kv + 1])
+            vv = host_f64(v[b:b + 1, kv:kv + 1])
+            cache[(b, kv)] = (oracle_dequant(*oracle_quantize(kk, "hd"), "hd")[0, 0],
+                              oracle_dequant(*oracle_quantize(vv, "hd"), "hd")[0, 0])
+        kd, vd = cache[(b, kv)]
+        hy = None
+        if hybrid_sets is not None:
+            toks, kr, vr = hybrid_sets[(b, kv)]
+            hy = {"tokens": toks, "k": kr, "v": vr, "q": host_f64(q_bf[b, h])}
+        res[(b, h)] = attention.decode_head(qd_all[b, h], kd, vd, int(ctx[b]), hybrid=hy)
+    return res
+
+
+def _compare(out, lse, ref, what):
+    o = out.cpu().numpy()
+    l = lse.cpu().numpy()
+    worst = 0.0
+    for (b, h), (ro, rl) in ref.items():
+        err = np.abs(o[b, h] - ro).max()
+        worst = max(worst, err)
+        assert err <= ATOL, f"{what}: (b={b}, h={h}) err {err:.3e}"
+        assert abs(l[b, h] - rl) <= 1e-3, f"{what}: lse (b={b}, h={h}) {l[b, h]} vs {rl}"
+    print(f"  {what}: worst |err| {worst:.3e} over {len(ref)} pairs", flush=True)
+
+
+@pytest.mark.parametrize("d, hq, hkv", [(128, 8, 2), (64, 4, 4), (128, 16, 2)])
+def test_decode_small_ragged(d, hq, hkv):
+    g = torch.Generator(device=DEV).manual_seed(31)
+    b, tcap = 2, 1000
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([1000, 577], dtype=torch.int32, device=DEV)
+    print(f"decode small d={d} hq={hq} hkv={hkv}", flush=True)
+    kc, vc = _cache(k, v)
+    qh = _query(q)
+    out, lse = mxa.decode(qh, kc, vc, ctx, split_len=256, return_lse=True)
+    torch.cuda.synchronize()
+    ref = _oracle_pair(q, k, v, ctx.cpu().numpy(), [(bb, h) for bb in range(b) for h in range(hq)])
+    _compare(out, lse, ref, f"decode d={d} G={hq // hkv}")
+
+
+def test_decode_split_and_tiny_context():
+    g = torch.Generator(device=DEV).manual_seed(32)
+    b, hq, hkv, tcap, d = 3, 4, 1, 700, 128
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([1, 64, 700], dtype=torch.int32, device=DEV)
+    kc, vc = _cache(k, v)
+    qh = _query(q)
+    outs = [mxa.decode(qh, kc, vc, ctx, split_len=s) for s in (64, 128, 2048)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() < 1e-5
+    ref = _oracle_pair(q, k, v, ctx.cpu().numpy(), [(bb, h) for bb in range(b) for h in range(hq)])
+    _compare(outs[0], mxa.decode(qh, kc, vc, ctx, split_len=64, return_lse=True)[1], ref, "split 64")
+    # ctx = 1: the output is the first value row.
+    vd = oracle_dequant(*oracle_quantize(host_f64(v[0:1, :, 0:1]), "hd"), "hd")[0, 0, 0]
+    np.testing.assert_allclose(outs[0][0, 0].cpu().numpy(), vd, atol=1e-6)
+
+
+def _hybrid_inputs(q, k, v, ctx, window, n_sel, max_sel, seed):
+    """Seeded selected sets (ascending, below ctx-window) and the gathered
+    bf16 rows the decode reads."""
+    rng = np.random.default_rng(seed)
+    b, hkv, tcap, d = k.shape
+    idx = np.full((b, hkv, max_sel), -1, dtype=np.int32)
+    nsel = np.zeros((b, hkv), dtype=np.int32)
+    sets = {}
+    kh, vh = host_f64(k), host_f64(v)
+    for bb in range(b):
+        c = int(ctx[bb])
+        lim = max(c - window, 0)
+        for h in range(hkv):
+            n = min(n_sel, lim)
+            sel = np.sort(rng.choice(lim, size=n, replace=False)) if n > 0 else np.zeros(0, np.int64)
+            idx[bb, h, :n] = sel
+            nsel[bb, h] = n
+            win = np.arange(max(c - window, 0), c)
+            toks = np.concatenate([sel, win]).astype(np.int64)
+            sets[(bb, h)] = (toks, kh[bb, h, toks], vh[bb, h, toks])
+    idx_t = torch.from_numpy(idx).to(DEV)
+    gidx = idx_t.clamp_min(0).long()
+    k_sel = torch.gather(k, 2, gidx[..., None].expand(-1, -1, -1, d)).contiguous()
+    v_sel = torch.gather(v, 2, gidx[..., None].expand(-1, -1, -1, d)).contiguous()
+    # Window rows: row w is token ctx - window + w (rows before token 0 unused).
+    k_win = torch.zeros((b, hkv, window, d), dtype=k.dtype, device=DEV)
+    v_win = torch.zeros_like(k_win)
+    for bb in range(b):
+        c = int(ctx[bb])
+        lo = max(c - window, 0)
+        k_win[bb, :, window - (c - lo):] = k[bb, :, lo:c]
+        v_win[bb, :, window - (c - lo):] = v[bb, :, lo:c]
+    hy = {"idx": idx_t, "n_sel": torch.from_numpy(nsel).to(DEV), "k_sel": k_sel, "v_sel": v_sel,
+          "k_win": k_win, "v_win": v_win, "window": window}
+    return hy, sets
+
+
+@pytest.mark.parametrize("window, n_sel", [(64, 40), (0, 0), (0, 30), (50, 0), (880, 10)])
+def test_hybrid_decode_small(window, n_sel):
+    g = torch.Generator(device=DEV).manual_seed(33)
+    b, hq, hkv, tcap, d = 2, 8, 2, 900, 128
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([900, 611], dtype=torch.int32, device=DEV)
+    print(f"hybrid small window={window} n_sel={n_sel}", flush=True)
+    kc, vc = _cache(k, v)
+    qh = _query(q)
+    max_sel = max(n_sel, 1) + 8
+    window_arg = min(window, tcap)
+    hy, sets = _hybrid_inputs(q, k, v, ctx.cpu().numpy(), window_arg, n_sel, max_sel, 7)
+    out, lse = mxa.decode(qh, kc, vc, ctx, split_len=128, hybrid=hy, q_bf16=q.contiguous(), return_lse=True)
+    torch.cuda.synchronize()
+    pairs = [(bb, h) for bb in range(b) for h in range(hq)]
+    ref = _oracle_pair(q, k, v, ctx.cpu().numpy(), pairs, hybrid_sets=sets, q_bf=q)
+    _compare(out, lse, ref, f"hybrid W={window} n={n_sel}")
+    if window == 0 and n_sel == 0:
+        plain = mxa.decode(qh, kc, vc, ctx, split_len=128)
+        torch.cuda.synchronize()
+        assert (plain - out).abs().max().item() < 1e-5
+
+
+def test_decode_workload_3_full_size():
+    """Batch 32, 32/8 heads, D=128, ctx 32768, split 2048: cache codes of the
+    sampled KV heads bit-exact, 12 sampled (b, hq) outputs vs the oracle."""
+    d = synth.long_decode(device=DEV)
+    print("decode workload-3 full", flush=True)
+    kc, vc = _cache(d["k"], d["v"])
+    qh = _query(d["q"])
+    out, lse = mxa.decode(qh, kc, vc, d["ctx_len"], split_len=2048, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    pairs = [(int(rng.integers(32)), int(rng.integers(32))) for _ in range(12)]
+    for (b, h) in pairs[:3]:
+        kv = h // 4
+        oc = oracle_quantize(host_f64(d["k"][b:b + 1, kv:kv + 1]), "hd")
+        sub = mxa.MX(kc.codes[b:b + 1, kv:kv + 1], kc.scales[b:b + 1, kv:kv + 1], (1, 1, 32768, 128), "hd")
+        assert_codes_equal(sub, *oc, f"cache b{b} kv{kv}")
+    ref = _oracle_pair(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), pairs)
+    _compare(out, lse, ref, "workload-3")
+
+
+def test_hybrid_decode_workload_4_full_size():
+    """Batch 8, 32/8 heads, ctx 32768, heavy-tailed column bias, window 128,
+    1632 selected tokens per KV head (seeded), rest MXFP4."""
+    d = synth.hybrid_decode(device=DEV)
+    print("hybrid decode workload-4 full", flush=True)
+    kc, vc = _cache(d["k"], d["v"])
+    qh = _query(d["q"])
+    hy, sets = _hybrid_inputs(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), 128, 1632, 1632, 9)
+    out, lse = mxa.decode(qh, kc, vc, d["ctx_len"], split_len=2048, hybrid=hy, q_bf16=d["q"].contiguous(),
+                          return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    pairs = [(int(rng.integers(8)), int(rng.integers(32))) for _ in range(8)]
+    ref = _oracle_pair(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), pairs, hybrid_sets=sets, q_bf=d["q"])
+    _compare(out, lse, ref, "workload-4 hybrid")
+
+
+# ------------------------------------------------------------------ selection
+def test_topk_exact_on_given_masses():
+    """R = 0: only the top-k runs, on integer-valued masses with many ties;
+    the indices must equal the oracle's exactly."""
+    rng = np.random.default_rng(41)
+    b, hkv, tcap = 3, 2, 5000
+    cm = rng.integers(0, 50, size=(b, hkv, tcap)).astype(np.float32)
+    ctx = np.array([5000, 3001, 129], dtype=np.int32)
+    kc = mxa.empty_mx((b, hkv, tcap, 128), "hd", DEV)
+    col = torch.from_numpy(cm).to(DEV)
+    idx, n = mxa.select_vertical(None, kc, torch.from_numpy(ctx).to(DEV), col, window=128,
+                                 rho_num=5, rho_den=100)
+    torch.cuda.synchronize()
+    for bb in range(b):
+        for h in range(hkv):
+            want = select.topk_vertical(cm[bb, h], int(ctx[bb]), 128, 5, 100)
+            got = idx[bb, h, : int(n[bb, h])].cpu().numpy()
+            np.testing.assert_array_equal(got, want)
+            assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
+
+
+def _check_selection(gpu_idx, gpu_n, oracle_cm, ctx, window, num, den, what):
+    k, nn = select.n_select(ctx, window, num, den)
+    assert gpu_n == k, f"{what}: count {gpu_n} vs {k}"
+    cm = oracle_cm[:nn]
+    order = np.sort(cm)[::-1]
+    tau = order[k - 1]
+    eps = 1e-4 * max(order[0], 1e-30)
+    got = set(gpu_idx.tolist())
+    assert len(got) == k and all(0 <= t < nn for t in got)
+    assert np.all(np.diff(gpu_idx) > 0), "indices must be ascending"
+    sure_in = set(np.nonzero(cm > tau + eps)[0].tolist())
+    assert sure_in <= got, f"{what}: {len(sure_in - got)} clearly heavier tokens missing"
+    assert all(cm[t] >= tau - eps for t in got), f"{what}: a clearly lighter token was selected"
+
+
+def test_select_vertical_workload_4():
+    """col_mass from 64 recent queries x 4 heads per KV head over ctx 32768,
+    then the top 5% of the non-window prefix; two calls accumulate."""
+    d = synth.hybrid_decode(device=DEV)
+    print("select workload-4 full", flush=True)
+    kc = mxa.quantize(d["k"], "hd")
+    qr = mxa.quantize(d["q_recent"], "hd")
+    col = torch.zeros((8, 8, 32768), dtype=torch.float32, device=DEV)
+    idx, n = mxa.select_vertical(qr, kc, d["ctx_len"], col, window=128)
+    torch.cuda.synchronize()
+    col1 = col.clone()
+    idx2, n2 = mxa.select_vertical(qr, kc, d["ctx_len"], col, window=128)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (3, 5), (7, 7)]:
+        kk = host_f64(d["k"][b:b + 1, h:h + 1])
+        kd = oracle_dequant(*oracle_quantize(kk, "hd"), "hd")[0, 0]
+        qq = host_f64(d["q_recent"][b:b + 1, 4 * h:4 * h + 4])
+        qd = oracle_dequant(*oracle_quantize(qq, "hd"), "hd")[0].reshape(-1, 128)
+        ocm = select.colmass_update(np.zeros(32768), qd, kd, 32768)
+        np.testing.assert_allclose(col1[b, h].cpu().numpy(), ocm, rtol=2e-4, atol=1e-7)
+        np.testing.assert_allclose(col[b, h].cpu().numpy(), 2 * ocm, rtol=2e-4, atol=2e-7)
+        _check_selection(idx[b, h, : int(n[b, h])].cpu().numpy(), int(n[b, h]), ocm, 32768, 128, 5, 100,
+                         f"select b{b} h{h}")
+        # The mass actually concentrates on few keys (vertical lines).
+        top = np.sort(ocm[:32640])[::-1]
+        frac = top[:1632].sum() / top.sum()
+        print(f"  b{b} h{h}: top-5% non-window mass fraction {frac:.3f}", flush=True)
