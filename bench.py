@@ -101,8 +101,8 @@ def prefill_leg(args):
 
 
 def prefill_cpu_baseline(d, cal):
-    """The oracle on 4 of the 32 query heads (one per distinct KV head pair),
-    every row: quantisation of those heads' Q, K, V plus the tiled prefill.
+    """The oracle on 11 of the 32 query heads (every third head), every row:
+    quantisation of those heads' Q, K, V plus the tiled prefill.
     Rate scaled to the full workload by the fraction of query-key pairs."""
     import numpy as np
     import torch
@@ -114,7 +114,7 @@ def prefill_cpu_baseline(d, cal):
     except Exception:
         blas_threads = os.cpu_count() or 1
     qs, ks = (c.cpu().numpy() for c in cal)
-    heads = [0, 9, 18, 27]
+    heads = list(range(0, 32, 3))
     q = d["q"][:, heads].float().cpu().numpy()
     k = d["k"].float().cpu().numpy()
     v = d["v"].to(torch.float64).cpu().numpy()
@@ -134,10 +134,139 @@ def prefill_cpu_baseline(d, cal):
     dt = time.perf_counter() - t0
     return {"value": 4 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"4 of 32 query heads, all 4096 rows (quantise + tiled PNQ prefill, float64 numpy; "
+            "sample": f"{len(heads)} of 32 query heads, all 4096 rows (quantise + tiled PNQ prefill, float64 numpy; "
                       f"{dt:.1f} s; BLAS threads {blas_threads}, elementwise single-threaded); "
                       f"rate scaled by pair count to the full workload",
             "seconds": dt}
+
+
+# ------------------------------------------------------------------ decode
+def _flush_buffer():
+    import torch
+    return torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+
+def timed_flushed(fn, steps, warmup, flush):
+    """Mean duration of fn over `steps` calls, each timed with events on the
+    current stream, with a 512 MB write between calls (not timed) so the
+    256 MB Infinity Cache holds none of the previous step's bytes."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    total = 0.0
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b) / 1e3
+    return total / steps
+
+
+def decode_leg(args, flush):
+    import torch
+    import bit_microscaled_flashattention_amd as mxa
+    import synth
+
+    B, HQ, HKV, T, D, SPLIT = 32, 32, 8, 32768, 128, 2048
+    d = synth.long_decode(device="cuda")
+    kc, vc = mxa.quantize(d["k"], "hd"), mxa.quantize(d["v"], "hd")
+    del d["k"], d["v"]
+    torch.cuda.empty_cache()
+    qh = mxa.empty_mx((B, HQ, 1, D), "hd")
+    ws = torch.empty(mxa.decode_workspace_bytes(B, HQ, HKV, D, T, SPLIT), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device="cuda")
+    q4 = d["q"][:, :, None, :]
+
+    def call():
+        mxa.decode(qh, kc, vc, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
+
+    def step():
+        mxa.quantize(q4, "hd", out=qh)
+        call()
+
+    t_call = timed_flushed(call, args.steps, args.warmup, flush)
+    t_step = timed_flushed(step, args.steps, args.warmup, flush)
+    cache_bytes = B * HKV * T * (D // 2 + D // 32) * 2
+    alg = cache_bytes + B * HQ * (D // 2 + D // 32) + B * HQ * D * 4
+    return {
+        "workload": "batch 32, 32/8 heads, head_dim 128, ctx 32768, MXFP4 K/V cache (E2M1 + E8M0 per 32 "
+                    "along head_dim), MXFP4 query, split 2048; step = quantise q + decode (scan + merge)",
+        "ms_per_token": round(t_step * 1e3, 4),
+        "GB_per_s": round(alg / t_step / 1e9, 1),
+        "algorithmic_bytes": alg,
+        "roofline": {"bound": "hbm", "kernel": "mxattn_decode (decode_fp4_kernel<128> + merge)",
+                     "achieved": round(alg / t_call / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(alg / t_call / 1e9 / PEAK_HBM_GBS, 4),
+                     "call_ms": round(t_call * 1e3, 4), "traffic": None},
+        "cache": "flushed (512 MB write) before every timed step",
+    }
+
+
+def hybrid_leg(args, flush):
+    import torch
+    import bit_microscaled_flashattention_amd as mxa
+    import synth
+
+    B, HQ, HKV, T, D, SPLIT, W = 8, 32, 8, 32768, 128, 2048, 128
+    d = synth.hybrid_decode(device="cuda")
+    kc, vc = mxa.quantize(d["k"], "hd"), mxa.quantize(d["v"], "hd")
+    qr = mxa.quantize(d["q_recent"], "hd")
+    col = torch.zeros((B, HKV, T), dtype=torch.float32, device="cuda")
+    sel_ws = torch.empty(mxa.select_workspace_bytes(B, HQ, 64, T), dtype=torch.uint8, device="cuda")
+
+    def select():
+        return mxa.select_vertical(qr, kc, d["ctx_len"], col, window=W, workspace=sel_ws)
+
+    idx, n = select()
+    # Gather the bf16 rows of the selected tokens and of the window (caller side).
+    max_sel = idx.shape[-1]
+    gidx = idx.clamp_min(0).long()[..., None].expand(-1, -1, -1, D)
+    hy = {"idx": idx, "n_sel": n, "window": W,
+          "k_sel": torch.gather(d["k"], 2, gidx).contiguous(), "v_sel": torch.gather(d["v"], 2, gidx).contiguous(),
+          "k_win": d["k"][:, :, T - W:].contiguous(), "v_win": d["v"][:, :, T - W:].contiguous()}
+    del d["k"], d["v"]
+    torch.cuda.empty_cache()
+    qh = mxa.empty_mx((B, HQ, 1, D), "hd")
+    ws = torch.empty(mxa.decode_workspace_bytes(B, HQ, HKV, D, T, SPLIT, True), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device="cuda")
+    q4 = d["q"][:, :, None, :]
+    qbf = d["q"].contiguous()
+
+    def call():
+        mxa.decode(qh, kc, vc, d["ctx_len"], split_len=SPLIT, hybrid=hy, q_bf16=qbf, workspace=ws, out=out)
+
+    def step():
+        mxa.quantize(q4, "hd", out=qh)
+        call()
+
+    t_call = timed_flushed(call, args.steps, args.warmup, flush)
+    t_step = timed_flushed(step, args.steps, args.warmup, flush)
+    t_sel = timed_flushed(select, max(args.steps // 4, 3), 1, flush)
+    nsel = int(n[0, 0].item())
+    n4 = T - W - nsel
+    per_pair = n4 * (D // 2 + D // 32) * 2 + (nsel + W) * D * 2 * 2 + nsel * 4 + (T + 31) // 32 * 4
+    alg = B * HKV * per_pair + B * HQ * (D // 2 + D // 32 + 2 * D) + B * HQ * D * 4
+    return {
+        "workload": "batch 8, 32/8 heads, head_dim 128, ctx 32768, heavy-tailed column bias; 1632 selected "
+                    "(top 5% of the non-window prefix by column mass) + 128-token window in bf16, rest MXFP4, "
+                    "one softmax; step = quantise q + hybrid decode",
+        "ms_per_token": round(t_step * 1e3, 4),
+        "GB_per_s": round(alg / t_step / 1e9, 1),
+        "algorithmic_bytes": alg,
+        "bf16_overhead_of_nonwindow_kv": round(nsel * (2 * D * 2 - (D // 2 + D // 32) * 2) /
+                                               ((T - W) * (D // 2 + D // 32) * 2), 4),
+        "selection_ms": round(t_sel * 1e3, 4),
+        "selection_share_of_64_steps": round(t_sel / (t_sel + 64 * t_step), 4),
+        "roofline": {"bound": "hbm", "kernel": "mxattn_decode hybrid (mask + fp4 scan + bf16 set + merge)",
+                     "achieved": round(alg / t_call / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(alg / t_call / 1e9 / PEAK_HBM_GBS, 4),
+                     "call_ms": round(t_call * 1e3, 4), "traffic": None},
+        "cache": "flushed (512 MB write) before every timed step",
+    }
 
 
 def main():
@@ -148,7 +277,6 @@ def main():
         sys.exit(2)
     import torch
     legs = set(args.legs.split(","))
-    out = {"metric": METRIC}
     pre, d, cal = prefill_leg(args)
     line = {
         "metric": METRIC,
@@ -174,6 +302,15 @@ def main():
     }
     del d
     torch.cuda.empty_cache()
+    if legs & {"decode", "hybrid"}:
+        flush = _flush_buffer()
+        if "decode" in legs:
+            line["decode"] = decode_leg(args, flush)
+            torch.cuda.empty_cache()
+        if "hybrid" in legs:
+            line["hybrid_decode"] = hybrid_leg(args, flush)
+            torch.cuda.empty_cache()
+        del flush
     if not args.no_cpu_baseline:
         d2 = __import__("synth").gqa_prefill(device="cuda")
         line["cpu_baseline"] = prefill_cpu_baseline(d2, cal)

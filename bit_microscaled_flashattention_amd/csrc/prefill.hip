@@ -42,20 +42,18 @@ struct Cfg {
   static constexpr int KB = BC / 32;        // 32-key blocks per tile
   static constexpr int DC = D / 64;         // 64-deep chunks of the QK^T contraction
   static constexpr int DT = D / 32;         // 32-channel tiles of O^T
-  static constexpr int KROW = D / 2 + 16;   // LDS bytes per K row (padded)
-  static constexpr int VROW = BC / 2 + 16;  // LDS bytes per V channel row (padded)
+  static constexpr int KRB = D / 2;         // bytes per K row (one key)
+  static constexpr int VRB = BC / 2;        // bytes per V row (one channel, BC keys)
   static constexpr int KSROW = D / 32;
   static constexpr int VSROW = BC / 32;
-  static constexpr int OFF_V = BC * KROW;
-  static constexpr int OFF_KS = OFF_V + D * VROW;
+  static constexpr int OFF_V = BC * KRB;
+  static constexpr int OFF_KS = OFF_V + D * VRB;
   static constexpr int OFF_VS = OFF_KS + BC * KSROW;
   static constexpr int STAGE = ((OFF_VS + D * VSROW) + 15) / 16 * 16;
-  static constexpr int NK16 = BC * D / 32;   // 16-byte chunks of K codes per tile
-  static constexpr int NV16 = D * BC / 32;   // 16-byte chunks of V codes per tile
-  static constexpr int NKS = BC * D / 32;    // K scale bytes per tile
-  static constexpr int NVS = D * BC / 32;    // V scale bytes per tile
-  static constexpr int IK = (NK16 + kThreads - 1) / kThreads;
-  static constexpr int IV = (NV16 + kThreads - 1) / kThreads;
+  static constexpr int K_LOADS = BC * KRB / 1024;  // 1 KB direct-to-LDS wave loads per tile
+  static constexpr int V_LOADS = D * VRB / 1024;
+  static constexpr int NKS = BC * D / 32;          // K scale bytes per tile
+  static constexpr int NVS = D * BC / 32;          // V scale bytes per tile
   static constexpr int IKS = (NKS + kThreads - 1) / kThreads;
   static constexpr int IVS = (NVS + kThreads - 1) / kThreads;
 };
@@ -64,97 +62,94 @@ struct Cfg {
 // that C row 8(r/4) + 4h + r%4 (lane half h, register r) is key 16h + r.
 __device__ __forceinline__ int sigma(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
+// LDS rows of RB bytes hold their 16-byte chunks XOR-swizzled by the row's
+// position inside a 256-byte bank period, so 16 lanes reading the same chunk
+// of 16 consecutive rows hit 16 different bank groups.
+template <int RB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  constexpr int rows_per_period = 256 / RB;
+  constexpr int chunks = RB / 16;
+  return chunk ^ ((row / rows_per_period) % chunks);
+}
+
 template <int D, int BC>
-struct Staged {
-  v4i kc[Cfg<D, BC>::IK];
-  v4i vc[Cfg<D, BC>::IV];
+struct ScaleRegs {
   uint8_t ks[Cfg<D, BC>::IKS];
   uint8_t vs[Cfg<D, BC>::IVS];
 };
 
+// Issue the direct HBM->LDS loads of a tile's K and V codes (this wave's
+// share of the 1 KB loads) and fetch its share of the scale bytes into
+// registers.  Rows past the sequence read a clamped valid row; their logits
+// are masked and their P is 0, so the bytes never matter.
 template <int D, int BC>
-__device__ __forceinline__ void load_tile(Staged<D, BC>& st, const PrefillArgs& a, int b, int hk, int t0,
-                                          int tid) {
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int hk, int t0, uint8_t* stage,
+                                           ScaleRegs<D, BC>& sr, int tid) {
   using C = Cfg<D, BC>;
+  const int wave = tid >> 6, lane = tid & 63;
   const uint8_t* kc = a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1];
   const uint8_t* ks = a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1];
   const uint8_t* vc = a.v.codes + b * a.v.cs[0] + hk * a.v.cs[1];
   const uint8_t* vs = a.v.scales + b * a.v.ss[0] + hk * a.v.ss[1];
-  const int nblk = (a.Sk + 31) / 32;  // 32-key blocks in a V row
+  const int nblk = (a.Sk + 31) / 32;
 #pragma unroll
-  for (int i = 0; i < C::IK; ++i) {
-    const int c = tid + kThreads * i;
-    v4i x = {0, 0, 0, 0};
-    if (c < C::NK16) {
-      const int row = c / (D / 32), part = c % (D / 32);
-      const int t = t0 + row;
-      if (t < a.Sk) x = *reinterpret_cast<const v4i*>(kc + t * a.k.cs[2] + part * 16);
-    }
-    st.kc[i] = x;
+  for (int i = wave; i < C::K_LOADS; i += 4) {
+    const int o = i * 1024 + 16 * lane;
+    const int r = o / C::KRB, pos = (o % C::KRB) / 16;
+    const int chunk = pos ^ ((r / (256 / C::KRB)) % (C::KRB / 16));
+    int t = t0 + (r & ~31) + sigma(r & 31);
+    t = t < a.Sk ? t : a.Sk - 1;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kc + t * a.k.cs[2] + chunk * 16),
+                                     (__attribute__((address_space(3))) void*)(stage + i * 1024),
+                                     16, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < C::IV; ++i) {
-    const int c = tid + kThreads * i;
-    v4i x = {0, 0, 0, 0};
-    if (c < C::NV16) {
-      const int d = c / (BC / 32), part = c % (BC / 32);
-      const int blk = t0 / 32 + part;
-      if (blk < nblk) x = *reinterpret_cast<const v4i*>(vc + d * a.v.cs[2] + blk * 16);
-    }
-    st.vc[i] = x;
+  for (int i = wave; i < C::V_LOADS; i += 4) {
+    const int o = i * 1024 + 16 * lane;
+    const int d = o / C::VRB, pos = (o % C::VRB) / 16;
+    const int chunk = pos ^ ((d / (256 / C::VRB)) % (C::VRB / 16));
+    int blk = t0 / 32 + chunk;
+    blk = blk < nblk ? blk : nblk - 1;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + d * a.v.cs[2] + blk * 16),
+                                     (__attribute__((address_space(3))) void*)(stage + C::OFF_V + i * 1024),
+                                     16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::IKS; ++i) {
     const int e = tid + kThreads * i;
     uint8_t x = 0;
     if (e < C::NKS) {
-      const int row = e / (D / 32), part = e % (D / 32);
-      const int t = t0 + row;
+      const int r = e / C::KSROW, part = e % C::KSROW;
+      const int t = t0 + (r & ~31) + sigma(r & 31);
       if (t < a.Sk) x = ks[t * a.k.ss[2] + part];
     }
-    st.ks[i] = x;
+    sr.ks[i] = x;
   }
 #pragma unroll
   for (int i = 0; i < C::IVS; ++i) {
     const int e = tid + kThreads * i;
     uint8_t x = 0;
     if (e < C::NVS) {
-      const int d = e / (BC / 32), part = e % (BC / 32);
+      const int d = e / C::VSROW, part = e % C::VSROW;
       const int blk = t0 / 32 + part;
       if (blk < nblk) x = vs[d * a.v.ss[2] + blk];
     }
-    st.vs[i] = x;
+    sr.vs[i] = x;
   }
 }
 
 template <int D, int BC>
-__device__ __forceinline__ void store_tile(const Staged<D, BC>& st, uint8_t* smem, int tid) {
+__device__ __forceinline__ void store_scales(const ScaleRegs<D, BC>& sr, uint8_t* stage, int tid) {
   using C = Cfg<D, BC>;
-#pragma unroll
-  for (int i = 0; i < C::IK; ++i) {
-    const int c = tid + kThreads * i;
-    if (c < C::NK16) {
-      const int row = c / (D / 32), part = c % (D / 32);
-      *reinterpret_cast<v4i*>(smem + row * C::KROW + part * 16) = st.kc[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < C::IV; ++i) {
-    const int c = tid + kThreads * i;
-    if (c < C::NV16) {
-      const int d = c / (BC / 32), part = c % (BC / 32);
-      *reinterpret_cast<v4i*>(smem + C::OFF_V + d * C::VROW + part * 16) = st.vc[i];
-    }
-  }
 #pragma unroll
   for (int i = 0; i < C::IKS; ++i) {
     const int e = tid + kThreads * i;
-    if (e < C::NKS) smem[C::OFF_KS + e] = st.ks[i];
+    if (e < C::NKS) stage[C::OFF_KS + e] = sr.ks[i];
   }
 #pragma unroll
   for (int i = 0; i < C::IVS; ++i) {
     const int e = tid + kThreads * i;
-    if (e < C::NVS) smem[C::OFF_VS + e] = st.vs[i];
+    if (e < C::NVS) stage[C::OFF_VS + e] = sr.vs[i];
   }
 }
 
@@ -186,7 +181,7 @@ __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int
 }
 
 template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, BC>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
   const int tid = threadIdx.x;
@@ -218,26 +213,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int my_nt = CAUSAL ? wave_last_q / BC + 1 : nt;
   const int wave_first_q = q0 + wave * 32;
 
-  // Two rows of E2M1 ones (rows 0 and 4: register 0 of both lane halves).
-  const bool one_row = (lane == 0 || lane == 4 || lane == 32 || lane == 36);
-  const int onev = one_row ? 0x22222222 : 0;
+  // E2M1 ones for the normaliser: a 16x16x128 A operand whose rows 0-7 sum
+  // the k-groups of lanes 0-15 and 32-47 (queries 0-15 of both key blocks)
+  // and rows 8-15 those of lanes 16-31 and 48-63 (queries 16-31).
+  const int one_r = lane & 15, one_kg = lane >> 4;
+  const bool one_on = (one_r < 8) ? (one_kg == 0 || one_kg == 2) : (one_kg == 1 || one_kg == 3);
+  const int onev = one_on ? 0x22222222 : 0;
   const v4i ones = {onev, onev, onev, onev};
+  const int l_query = (lane & 15) + 16 * (lane >> 5);
 
   float m = -__builtin_huge_valf();
   float lsum = 0.0f;  // baseline normaliser (sum of unquantised P~)
   v16f O[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) O[dt] = v16f{};
-  v16f L = v16f{};
+  v4f L = v4f{0, 0, 0, 0};
 
-  Staged<D, BC> st;
-  load_tile<D, BC>(st, a, b, hk, 0, tid);
-  store_tile<D, BC>(st, smem, tid);
+  ScaleRegs<D, BC> sr;
+  issue_tile<D, BC>(a, b, hk, 0, smem, sr, tid);
+  store_scales<D, BC>(sr, smem, tid);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int jt = 0; jt < nt; ++jt) {
     const int t0 = jt * BC;
-    if (jt + 1 < nt) load_tile<D, BC>(st, a, b, hk, t0 + BC, tid);
+    uint8_t* next = smem + ((jt + 1) & 1) * C::STAGE;
+    if (jt + 1 < nt) issue_tile<D, BC>(a, b, hk, t0 + BC, next, sr, tid);
     if (jt < my_nt) {
       const uint8_t* base = smem + (jt & 1) * C::STAGE;
       const uint8_t* Kc = base;
@@ -249,12 +250,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       v16f S[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        const int krow = kb * 32 + sigma(j);
+        const int r = kb * 32 + j;
         v16f acc = v16f{};
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) {
-          const v4i aop = *reinterpret_cast<const v4i*>(Kc + krow * C::KROW + dc * 32 + hh * 16);
-          const int sa = Ks[krow * C::KSROW + 2 * dc + hh];
+          const v4i aop = *reinterpret_cast<const v4i*>(Kc + r * C::KRB + 16 * swz<C::KRB>(r, 2 * dc + hh));
+          const int sa = Ks[r * C::KSROW + 2 * dc + hh];
           acc = mfma32_fp4(aop, qop[dc], acc, sa, qsc[dc]);
         }
         S[kb] = acc;
@@ -291,9 +292,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       const float alpha = fast_exp2((m - m_new) * a.c);
       const float mc = m_new * a.c;
 
-      // ---- P~, its MXFP4 codes, and the B operands of the PV product
-      v4i bop[C::KB / 2];
-      int bsc[C::KB / 2];
+      // ---- P~ (in place of S), its MXFP4 codes, the PV B operands
       uint32_t code[C::KB][2];
       int eb[C::KB];
       float tile_sum = 0.0f;
@@ -304,13 +303,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         byte = byte < 1 ? 1 : byte;  // keep the convert's scale a normal float
         eb[kb] = byte;
         const float scl = scale_of_byte(byte);
-        float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(S[kb][r], a.c, -mc));
+        for (int r = 0; r < 16; ++r) S[kb][r] = fast_exp2(__builtin_fmaf(S[kb][r], a.c, -mc));
         if (!a.l_from_quantized) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tile_sum += p[r];
+          for (int r = 0; r < 16; ++r) tile_sum += S[kb][r];
         }
+        const v16f& p = S[kb];
         uint32_t w0 = 0, w1 = 0;
         w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[0], p[1], scl, 0);
         w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
@@ -323,13 +322,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         code[kb][0] = w0;
         code[kb][1] = w1;
       }
-#pragma unroll
-      for (int pp = 0; pp < C::KB / 2; ++pp) {
-        const auto r0 = __builtin_amdgcn_permlane32_swap(code[2 * pp][0], code[2 * pp + 1][0], false, false);
-        const auto r1 = __builtin_amdgcn_permlane32_swap(code[2 * pp][1], code[2 * pp + 1][1], false, false);
-        bop[pp] = v4i{(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
-        bsc[pp] = hh ? eb[2 * pp + 1] : eb[2 * pp];
-      }
       if (!a.l_from_quantized) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tile_sum), __float_as_uint(tile_sum), false, false);
         lsum = alpha * lsum + (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
@@ -338,33 +330,40 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       // ---- rescale the accumulators (skipped when no row's maximum moved)
       if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-        L[0] *= alpha;
+        for (int dt = 0; dt < C::DT; ++dt) O[dt] *= alpha;
+        // L[0] of this lane is the normaliser of query l%16 + 16*(l/32),
+        // whose factor lives in that query's lane.
+        L[0] *= __shfl(alpha, l_query);
       }
       m = m_new;
 
       // ---- O^T += V_hat^T P_hat^T, and l += ones^T P_hat^T
 #pragma unroll
       for (int pp = 0; pp < C::KB / 2; ++pp) {
+        const auto r0 = __builtin_amdgcn_permlane32_swap(code[2 * pp][0], code[2 * pp + 1][0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(code[2 * pp][1], code[2 * pp + 1][1], false, false);
+        const v4i bop = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
+        const int bsc = hh ? eb[2 * pp + 1] : eb[2 * pp];
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const int vrow = dt * 32 + j;
-          const v4i aop = *reinterpret_cast<const v4i*>(Vc + vrow * C::VROW + pp * 32 + hh * 16);
+          const v4i aop = *reinterpret_cast<const v4i*>(Vc + vrow * C::VRB + 16 * swz<C::VRB>(vrow, 2 * pp + hh));
           const int sa = Vs[vrow * C::VSROW + 2 * pp + hh];
-          O[dt] = mfma32_fp4(aop, bop[pp], O[dt], sa, bsc[pp]);
+          O[dt] = mfma32_fp4(aop, bop, O[dt], sa, bsc);
         }
-        L = mfma32_fp4(ones, bop[pp], L, a.one_scale, bsc[pp]);
+        L = mfma16_fp4(ones, bop, L, a.one_scale, bsc);
       }
     }
-    if (jt + 1 < nt) store_tile<D, BC>(st, smem + ((jt + 1) & 1) * C::STAGE, tid);
+    if (jt + 1 < nt) store_scales<D, BC>(sr, next, tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // ---- finalise: out = O / l, lse = m * softmax_scale + ln l
+  // The normaliser of query j sits in lane j (j < 16) or j + 16 (j >= 16).
+  const float lq = __shfl(L[0], j < 16 ? j : j + 16);
   if (my_q >= a.Sq) return;
-  const float l = a.l_from_quantized ? L[0] : lsum;
+  const float l = a.l_from_quantized ? lq : lsum;
   const float inv = 1.0f / l;
   const int64_t orow = (static_cast<int64_t>(b) * a.Hq + hq) * a.Sq + my_q;
   if (a.lse != nullptr && hh == 0) a.lse[orow] = m * a.softmax_scale + logf(l);
