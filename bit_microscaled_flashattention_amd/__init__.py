@@ -213,8 +213,9 @@ def prefill(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, p_rule="ocp",
     return (out, lse) if return_lse else out
 
 
-def decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, hybrid=False):
-    return int(_lib.mxattn_decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, int(hybrid)))
+def decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, hybrid_rows=0):
+    """Workspace of decode(); hybrid_rows = max_sel + window of the hybrid set."""
+    return int(_lib.mxattn_decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, int(hybrid_rows)))
 
 
 def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybrid=None,
@@ -227,7 +228,8 @@ def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybr
     b, hq, _, d = q.shape
     hkv, tcap = k_cache.shape[1], k_cache.shape[2]
     dev = q.codes.device
-    need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hybrid is not None)
+    hy_rows = (hybrid["idx"].shape[-1] + int(hybrid["window"])) if hybrid is not None else 0
+    need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hy_rows)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:

@@ -241,13 +241,19 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
   return after_launch(launch_prefill(a, static_cast<int>(q->dim), kv_tile, p->causal != 0, s), s, "prefill");
 }
 
+// Rows of the bf16 hybrid set handled per partial slot (one workgroup each).
+static constexpr int64_t kBf16Rows = 256;
+static constexpr int64_t kMaxSlots = 4096;
+
+static int64_t bf16_slots(int64_t hybrid_rows) { return hybrid_rows > 0 ? (hybrid_rows + kBf16Rows - 1) / kBf16Rows : 0; }
+
 size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int64_t dim, int64_t tcap,
-                                     int32_t split_len, int32_t hybrid) {
-  if (batch < 1 || hq < 1 || hkv < 1 || dim < 1 || tcap < 1 || split_len < 1) return 0;
-  const int64_t n_split = (tcap + split_len - 1) / split_len + (hybrid ? 1 : 0);
-  size_t bytes = static_cast<size_t>(batch * hq * n_split * (dim + 2)) * sizeof(float);
+                                     int32_t split_len, int32_t hybrid_rows) {
+  if (batch < 1 || hq < 1 || hkv < 1 || dim < 1 || tcap < 1 || split_len < 1 || hybrid_rows < 0) return 0;
+  const int64_t n_slot = (tcap + split_len - 1) / split_len + bf16_slots(hybrid_rows);
+  size_t bytes = static_cast<size_t>(batch * hq * n_slot * (dim + 2)) * sizeof(float);
   bytes = (bytes + 255) / 256 * 256;
-  if (hybrid) bytes += static_cast<size_t>(batch * hkv * ((tcap + 31) / 32)) * sizeof(uint32_t);
+  if (hybrid_rows > 0) bytes += static_cast<size_t>(batch * hkv * ((tcap + 31) / 32)) * sizeof(uint32_t);
   return bytes;
 }
 
@@ -283,7 +289,12 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
     if (hy->max_sel + static_cast<int64_t>(hy->window) > kc->seq)
       return fail(MXATTN_ERR_INVALID_ARG, "decode: max_sel + window exceeds the cache");
   }
-  const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, kc->seq, split_len, hybrid);
+  const int64_t hybrid_rows = hybrid ? static_cast<int64_t>(hy->max_sel) + hy->window : 0;
+  const int64_t n_split = (kc->seq + split_len - 1) / split_len;
+  if (n_split + bf16_slots(hybrid_rows) > kMaxSlots)
+    return fail(MXATTN_ERR_UNSUPPORTED, "decode: more than %lld partial slots; use a longer split_len", (long long)kMaxSlots);
+  const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, kc->seq, split_len,
+                                                    static_cast<int32_t>(hybrid_rows));
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MXATTN_ERR_WORKSPACE, "decode: workspace of %zu bytes needed", need);
   if (!aligned16(workspace)) return fail(MXATTN_ERR_INVALID_ARG, "decode: workspace not 16-byte aligned");
@@ -300,7 +311,8 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
   a.softmax_scale = sm;
   a.c = sm * 1.4426950408889634f;
   a.split_len = split_len;
-  a.n_split = static_cast<int>((kc->seq + split_len - 1) / split_len);
+  a.n_split = static_cast<int>(n_split);
+  a.n_bf16 = static_cast<int>(bf16_slots(hybrid_rows));
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.lse = lse;
@@ -315,7 +327,7 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
     a.v_sel = static_cast<const uint16_t*>(hy->v_sel);
     a.k_win = static_cast<const uint16_t*>(hy->k_win);
     a.v_win = static_cast<const uint16_t*>(hy->v_win);
-    size_t part_bytes = static_cast<size_t>(a.B) * a.Hq * (a.n_split + 1) * (q->dim + 2) * sizeof(float);
+    size_t part_bytes = static_cast<size_t>(a.B) * a.Hq * (a.n_split + a.n_bf16) * (q->dim + 2) * sizeof(float);
     part_bytes = (part_bytes + 255) / 256 * 256;
     a.mask = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + part_bytes);
   }

@@ -18,8 +18,8 @@
 //     significant bits).  V rows are converted to bf16 with their scale
 //     (v_cvt_scalef32_pk_bf16_fp4, exact) and staged in LDS, from where each
 //     lane gathers the 8 tokens of its channel for the V^T operand.
-//   * The next chunk's K and V bytes are loaded while the current one is
-//     computed.  Partial (O, m, l) per split go to the workspace and a merge
+//   * The next chunks' K and V bytes are loaded (non-temporal: the cache is
+//     streamed once) while the current one is computed.  Partial (O, m, l) per split go to the workspace and a merge
 //     kernel combines them in a fixed order (deterministic).
 #include "mx_device.h"
 #include "kernels.h"
@@ -31,6 +31,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kDecThreads = 256;
 constexpr int kChunk = 32;          // tokens per wave iteration
 constexpr int kVRow = 256 + 16;     // LDS bytes per staged bf16 V row (128 ch + pad)
+constexpr int kBf16Rows = 256;      // bf16 hybrid rows per workgroup
+constexpr int kMaxSlots = 4096;     // partial slots per (batch, query head) the merge handles
 
 __device__ __forceinline__ v4f mfma16_bf16(v4i a, v4i b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
@@ -57,7 +59,7 @@ struct DecState {
 // this lane's 8 tokens for query column j.  Produces the hi/lo bf16 B
 // operands of the PV product.
 __device__ __forceinline__ void softmax_chunk(DecState& st, const float* s, float c, v4i& bhi, v4i& blo,
-                                              float& alpha) {
+                                              float& alpha, bool& moved) {
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
@@ -67,6 +69,7 @@ __device__ __forceinline__ void softmax_chunk(DecState& st, const float* s, floa
   // m_new = -inf only while nothing has been seen: keep the state at zero.
   const bool none = m_new == -__builtin_huge_valf();
   alpha = none ? 1.0f : fast_exp2((st.m - m_new) * c);
+  moved = __builtin_amdgcn_ballot_w64(m_new > st.m) != 0;
   const float mc = none ? 0.0f : m_new * c;
   float p[8];
   float sum = 0.0f;
@@ -91,8 +94,13 @@ __device__ __forceinline__ void softmax_chunk(DecState& st, const float* s, floa
 
 // O^T += V^T P^T for one chunk from the staged bf16 rows (this wave's LDS).
 __device__ __forceinline__ void pv_chunk(DecState& st, const uint8_t* vr, int lane, v4i bhi, v4i blo, float alpha,
-                                         int D) {
+                                         bool moved, int D) {
   const int dl = lane & 15, g = lane >> 4;
+  if (moved) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      if (dt * 16 < D) st.O[dt] *= alpha;
+  }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     if (dt * 16 >= D) break;
@@ -105,8 +113,7 @@ __device__ __forceinline__ void pv_chunk(DecState& st, const uint8_t* vr, int la
       w[i] = a | (b << 16);
     }
     const v4i aop = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    v4f o = st.O[dt] * alpha;
-    o = mfma16_bf16(aop, bhi, o);
+    const v4f o = mfma16_bf16(aop, bhi, st.O[dt]);
     st.O[dt] = mfma16_bf16(aop, blo, o);
   }
 }
@@ -159,9 +166,54 @@ constexpr int kStageBytes = 4 * kChunk * kVRow;
 static_assert(sizeof(RedLds) <= kStageBytes, "reduction must fit in the staging area");
 
 // ---------------------------------------------------------------------------
-// FP4 cache scan of one split.
+// Per-lane bytes of one 32-token chunk: the K operands of the two 16-key
+// logit tiles and two (token, 32-channel) V blocks for the bf16 staging.
+struct ChunkRegs {
+  v4i k[2];
+  int ks[2];
+  v4i v[2];
+  int vs[2];
+};
+
+// Make this wave's LDS writes visible to its own later reads (LDS requests of
+// one wave execute in order; the wait also keeps the compiler from moving
+// the reads above it).
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Convert the chunk's V blocks to bf16 rows (exact: code x 2^e) in the wave's
+// staging rows.
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void decode_fp4_kernel(DecodeArgs a) {
+__device__ __forceinline__ void stage_v(const ChunkRegs& r, uint8_t* vr, int lane) {
+  constexpr int nblk_d = D / 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int bi = lane + 64 * h;
+    const int tt = bi / nblk_d, db = bi % nblk_d;
+    if (tt < kChunk) {
+      const float scl = r.vs[h] > 0 ? scale_of_byte(r.vs[h]) : 0.0f;
+      uint32_t w[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t src = static_cast<uint32_t>(r.v[h][q]);
+        w[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0));
+        w[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1));
+        w[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2));
+        w[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3));
+      }
+      uint8_t* dst = vr + tt * kVRow + db * 64;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<v4i*>(dst + 16 * q) = v4i{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]};
+    }
+  }
+}
+
+// FP4 cache scan of one split.  Each wave streams its own chunks (wave w
+// takes chunks w, w+4, ...) with two chunks of loads in flight, through its
+// own LDS staging rows, so the waves never wait for each other until the
+// final combine.
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -173,19 +225,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_fp4_kernel(DecodeArgs a) {
   const int end4 = ctx - win;                    // 4-bit tokens are [0, end4)
   const int t_begin = split * a.split_len;
   const int t_end = min(t_begin + a.split_len, end4);
-  const int n_slot = a.n_split + (a.hybrid ? 1 : 0);
 
   // Query operand: column j (query head hk*G + j), channels [32g, 32g+32).
   v4i qop = {0, 0, 0, 0};
   int qsc = 0;
-  if (j < G) {
+  if (j < G && g < D / 32) {
     const int hq = hk * G + j;
     const uint8_t* qc = a.q.codes + b * a.q.cs[0] + hq * a.q.cs[1];
     const uint8_t* qs = a.q.scales + b * a.q.ss[0] + hq * a.q.ss[1];
-    if (g < D / 32) {
-      qop = *reinterpret_cast<const v4i*>(qc + g * 16);
-      qsc = qs[g];
-    }
+    qop = *reinterpret_cast<const v4i*>(qc + g * 16);
+    qsc = qs[g];
   }
   const uint8_t* kc = a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1];
   const uint8_t* ks = a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1];
@@ -200,98 +249,74 @@ __global__ __launch_bounds__(kDecThreads) void decode_fp4_kernel(DecodeArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.O[dt] = v4f{0, 0, 0, 0};
 
-  const int nblk_d = D / 32;
-  // Per-lane loads of one chunk: K operands of the two 16-key tiles, and two
-  // (token, 32-channel) V blocks for the bf16 staging.
-  struct Loaded {
-    v4i k[2];
-    int ks[2];
-    v4i v[2];
-    int vs[2];
-  } cur, nxt;
-  auto load = [&](Loaded& L, int t0) {
+  constexpr int nblk_d = D / 32;
+  auto load = [&](ChunkRegs& r, int t0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = t0 + h * 16 + j;
       const bool ok = t < t_end && g < nblk_d;
-      L.k[h] = ok ? *reinterpret_cast<const v4i*>(kc + static_cast<int64_t>(t) * a.k.cs[2] + g * 16) : v4i{0, 0, 0, 0};
-      L.ks[h] = ok ? ks[static_cast<int64_t>(t) * a.k.ss[2] + g] : 0;
+      r.k[h] = ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(kc + static_cast<int64_t>(t) * a.k.cs[2] + g * 16))
+                  : v4i{0, 0, 0, 0};
+      r.ks[h] = ok ? ks[static_cast<int64_t>(t) * a.k.ss[2] + g] : 0;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int bi = lane + 64 * h;               // (token, channel block) id in the chunk
+      const int bi = lane + 64 * h;
       const int tt = bi / nblk_d, db = bi % nblk_d;
       const int t = t0 + tt;
       const bool ok = tt < kChunk && t < t_end;
-      L.v[h] = ok ? *reinterpret_cast<const v4i*>(vc + static_cast<int64_t>(t) * a.v.cs[2] + db * 16) : v4i{0, 0, 0, 0};
-      L.vs[h] = ok ? vs[static_cast<int64_t>(t) * a.v.ss[2] + db] : 127;
+      r.v[h] = ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vc + static_cast<int64_t>(t) * a.v.cs[2] + db * 16))
+                  : v4i{0, 0, 0, 0};
+      r.vs[h] = ok ? vs[static_cast<int64_t>(t) * a.v.ss[2] + db] : 127;
     }
+  };
+  auto process = [&](const ChunkRegs& r, int t0) {
+    stage_v<D>(r, vr, lane);
+    const v4f s0 = mfma16_fp4(r.k[0], qop, v4f{0, 0, 0, 0}, r.ks[0], qsc);
+    const v4f s1 = mfma16_fp4(r.k[1], qop, v4f{0, 0, 0, 0}, r.ks[1], qsc);
+    float sv[8];
+    const uint32_t mw = mask ? mask[t0 / 32] : 0u;   // chunks are 32-aligned
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tk = chunk_tok(g, i);
+      const float x = i < 4 ? s0[i] : s1[i - 4];
+      const bool absent = (t0 + tk >= t_end) || ((mw >> tk) & 1u) || j >= G;
+      sv[i] = absent ? -__builtin_huge_valf() : x;
+    }
+    v4i bhi, blo;
+    float alpha;
+    bool moved;
+    softmax_chunk(st, sv, a.c, bhi, blo, alpha, moved);
+    wave_lds_sync();
+    pv_chunk(st, vr, lane, bhi, blo, alpha, moved, D);
   };
 
   const int n_chunks = t_end > t_begin ? (t_end - t_begin + kChunk - 1) / kChunk : 0;
-  const int rounds = (n_chunks + 3) / 4;
-  if (rounds > 0) load(cur, t_begin + wave * kChunk);
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int ci = rd * 4 + wave;
-    const int t0 = t_begin + ci * kChunk;
-    const bool active = ci < n_chunks;
-    if (rd + 1 < rounds) load(nxt, t0 + 4 * kChunk);
-    // Stage V as bf16 rows (exact: code x 2^e).
-    if (active) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int bi = lane + 64 * h;
-        const int tt = bi / nblk_d, db = bi % nblk_d;
-        if (tt < kChunk) {
-          const float scl = cur.vs[h] > 0 ? scale_of_byte(cur.vs[h]) : 0.0f;
-          uint32_t w[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t src = static_cast<uint32_t>(cur.v[h][q]);
-            w[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 0));
-            w[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 1));
-            w[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 2));
-            w[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scl, 3));
-          }
-          uint8_t* dst = vr + tt * kVRow + db * 64;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<v4i*>(dst + 16 * q) = v4i{(int)w[4 * q], (int)w[4 * q + 1], (int)w[4 * q + 2], (int)w[4 * q + 3]};
-        }
-      }
+  const int mine = n_chunks > wave ? (n_chunks - wave + 3) / 4 : 0;   // chunks of this wave
+  ChunkRegs A, B;
+  auto chunk_t0 = [&](int i) { return t_begin + (wave + 4 * i) * kChunk; };
+  if (mine > 0) load(A, chunk_t0(0));
+  if (mine > 1) load(B, chunk_t0(1));
+  for (int i = 0; i < mine; i += 2) {
+    process(A, chunk_t0(i));
+    if (i + 2 < mine) load(A, chunk_t0(i + 2));
+    if (i + 1 < mine) {
+      process(B, chunk_t0(i + 1));
+      if (i + 3 < mine) load(B, chunk_t0(i + 3));
     }
-    __syncthreads();
-    if (active) {
-      // Logits for the two 16-key tiles.
-      v4f s0 = mfma16_fp4(cur.k[0], qop, v4f{0, 0, 0, 0}, cur.ks[0], qsc);
-      v4f s1 = mfma16_fp4(cur.k[1], qop, v4f{0, 0, 0, 0}, cur.ks[1], qsc);
-      float s[8];
-      const uint32_t mw = mask ? mask[t0 / 32] : 0u;   // chunks are 32-aligned
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tk = chunk_tok(g, i);
-        const float x = i < 4 ? s0[i] : s1[i - 4];
-        const bool absent = (t0 + tk >= t_end) || ((mw >> tk) & 1u) || j >= G;
-        s[i] = absent ? -__builtin_huge_valf() : x;
-      }
-      v4i bhi, blo;
-      float alpha;
-      softmax_chunk(st, s, a.c, bhi, blo, alpha);
-      pv_chunk(st, vr, lane, bhi, blo, alpha, D);
-    }
-    __syncthreads();
-    cur = nxt;
   }
-
-  combine_store<D>(vstage, st, a, b, hk, split, n_slot);
+  __syncthreads();
+  combine_store<D>(vstage, st, a, b, hk, split, a.n_split + a.n_bf16);
 }
 
 // ---------------------------------------------------------------------------
-// bf16 hybrid set: selected rows (idx < ctx - window) then the window rows.
+// bf16 hybrid set: the selected rows (those below ctx - window) followed by
+// the window rows, kBf16Rows rows per workgroup (blockIdx.x), each result in
+// its own partial slot after the 4-bit splits.
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
-  const int hk = blockIdx.y, b = blockIdx.z;
+  const int part_id = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.Hq / a.Hkv;
@@ -305,8 +330,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   // Selected rows at or past ctx - window are not part of the set.
   const int limit = ctx - win;
   const int n_total = nsel + win;
-  const int woff = a.window - win;   // window rows before ctx-window+0 are unused
-  const int n_slot = a.n_split + 1;
+  const int woff = a.window - win;   // window rows before token 0 are unused
+  const int r_begin = part_id * kBf16Rows;
+  const int r_end = min(r_begin + kBf16Rows, n_total);
   uint8_t* vr = vstage + wave * kChunk * kVRow;
 
   // bf16 query operand for the 16x16x32 bf16 MFMA: column j, channels
@@ -326,7 +352,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   auto row_v = [&](int i) -> const uint16_t* {
     return i < nsel ? a.v_sel + (bh * a.max_sel + i) * D : a.v_win + (bh * a.window + woff + (i - nsel)) * D;
   };
-  auto valid = [&](int i) -> bool { return i < n_total && (i >= nsel || idx[i] < limit); };
+  auto valid = [&](int i) -> bool { return i < r_end && (i >= nsel || idx[i] < limit); };
 
   DecState st;
   st.m = -__builtin_huge_valf();
@@ -334,54 +360,45 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.O[dt] = v4f{0, 0, 0, 0};
 
-  const int n_chunks = (n_total + kChunk - 1) / kChunk;
-  const int rounds = (n_chunks + 3) / 4;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int ci = rd * 4 + wave;
-    const int t0 = ci * kChunk;
-    const bool active = ci < n_chunks;
-    if (active) {
-      // Stage V rows: 32 rows x D bf16, 16 bytes per lane per step.
-      for (int e = lane; e < kChunk * (D / 8); e += 64) {
-        const int tt = e / (D / 8), part = e % (D / 8);
-        v4i x = {0, 0, 0, 0};
-        if (t0 + tt < n_total) x = *reinterpret_cast<const v4i*>(row_v(t0 + tt) + part * 8);
-        *reinterpret_cast<v4i*>(vr + tt * kVRow + part * 16) = x;
-      }
+  // Wave w takes the chunks r_begin + 32 (w + 4 i).
+  for (int t0 = r_begin + wave * kChunk; t0 < r_end; t0 += 4 * kChunk) {
+    for (int e = lane; e < kChunk * (D / 8); e += 64) {
+      const int tt = e / (D / 8), part = e % (D / 8);
+      v4i x = {0, 0, 0, 0};
+      if (t0 + tt < r_end) x = *reinterpret_cast<const v4i*>(row_v(t0 + tt) + part * 8);
+      *reinterpret_cast<v4i*>(vr + tt * kVRow + part * 16) = x;
     }
-    __syncthreads();
-    if (active) {
-      v4f sc[2];
+    v4f sc[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int i = t0 + h * 16 + j;
-        const bool ok = i < n_total;
-        const uint16_t* kr = ok ? row_k(i) : nullptr;
-        v4f acc = {0, 0, 0, 0};
+    for (int h = 0; h < 2; ++h) {
+      const int i = t0 + h * 16 + j;
+      const bool ok = i < r_end;
+      const uint16_t* kr = ok ? row_k(i) : nullptr;
+      v4f acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          if (kk * 32 >= D) break;
-          const v4i aop = ok ? *reinterpret_cast<const v4i*>(kr + kk * 32 + 8 * g) : v4i{0, 0, 0, 0};
-          acc = mfma16_bf16(aop, qop[kk], acc);
-        }
-        sc[h] = acc;
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk * 32 >= D) break;
+        const v4i aop = ok ? *reinterpret_cast<const v4i*>(kr + kk * 32 + 8 * g) : v4i{0, 0, 0, 0};
+        acc = mfma16_bf16(aop, qop[kk], acc);
       }
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tk = chunk_tok(g, i);
-        const float x = i < 4 ? sc[0][i] : sc[1][i - 4];
-        s[i] = (valid(t0 + tk) && j < G) ? x : -__builtin_huge_valf();
-      }
-      v4i bhi, blo;
-      float alpha;
-      softmax_chunk(st, s, a.c, bhi, blo, alpha);
-      pv_chunk(st, vr, lane, bhi, blo, alpha, D);
+      sc[h] = acc;
     }
-    __syncthreads();
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tk = chunk_tok(g, i);
+      const float x = i < 4 ? sc[0][i] : sc[1][i - 4];
+      sv[i] = (valid(t0 + tk) && j < G) ? x : -__builtin_huge_valf();
+    }
+    v4i bhi, blo;
+    float alpha;
+    bool moved;
+    softmax_chunk(st, sv, a.c, bhi, blo, alpha, moved);
+    wave_lds_sync();
+    pv_chunk(st, vr, lane, bhi, blo, alpha, moved, D);
   }
-
-  combine_store<D>(vstage, st, a, b, hk, a.n_split, n_slot);
+  __syncthreads();
+  combine_store<D>(vstage, st, a, b, hk, a.n_split + part_id, a.n_split + a.n_bf16);
 }
 
 // ---------------------------------------------------------------------------
@@ -409,26 +426,52 @@ __global__ __launch_bounds__(256) void hybrid_mask_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials, in split order.
+// Log-sum-exp merge of the partial slots, in slot order.  One workgroup per
+// (batch, query head): the slots' (m, l) go through LDS once, then every
+// channel sums its weighted partials with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float wgt[kMaxSlots];
+  __shared__ float s_den, s_m;
   const int hq = blockIdx.x, b = blockIdx.y;
   const int d = threadIdx.x;
-  const int n_slot = a.n_split + (a.hybrid ? 1 : 0);
+  const int n_slot = a.n_split + a.n_bf16;
   const float* p = a.part + (static_cast<int64_t>(b) * a.Hq + hq) * n_slot * (D + 2);
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < n_slot; ++s) M = fmaxf(M, p[s * (D + 2) + D]);
-  float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < n_slot; ++s) {
-    const float ms = p[s * (D + 2) + D];
-    if (ms == -__builtin_huge_valf()) continue;
-    const float f = fast_exp2((ms - M) * a.c);
-    num += f * p[s * (D + 2) + d];
-    den += f * p[s * (D + 2) + D + 1];
+  if (d < 64) {
+    // One wave: maximum and weights of all slots.
+    float M = -__builtin_huge_valf();
+    for (int s = d; s < n_slot; s += 64) M = fmaxf(M, p[s * (D + 2) + D]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float den = 0.0f;
+    for (int s = d; s < n_slot; s += 64) {
+      const float ms = p[s * (D + 2) + D];
+      const float w = ms == -__builtin_huge_valf() ? 0.0f : fast_exp2((ms - M) * a.c);
+      wgt[s] = w;
+      den += w * p[s * (D + 2) + D + 1];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    if (d == 0) {
+      s_den = den;
+      s_m = M;
+    }
   }
+  __syncthreads();
+  float num = 0.0f;
+  int s = 0;
+  for (; s + 4 <= n_slot; s += 4) {
+    const float x0 = p[(s + 0) * (D + 2) + d], x1 = p[(s + 1) * (D + 2) + d];
+    const float x2 = p[(s + 2) * (D + 2) + d], x3 = p[(s + 3) * (D + 2) + d];
+    num += wgt[s] * x0;
+    num += wgt[s + 1] * x1;
+    num += wgt[s + 2] * x2;
+    num += wgt[s + 3] * x3;
+  }
+  for (; s < n_slot; ++s) num += wgt[s] * p[s * (D + 2) + d];
   const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
-  a.out[row * D + d] = num / den;
-  if (a.lse != nullptr && d == 0) a.lse[row] = M * a.softmax_scale + logf(den);
+  a.out[row * D + d] = num / s_den;
+  if (a.lse != nullptr && d == 0) a.lse[row] = s_m * a.softmax_scale + logf(s_den);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {
@@ -437,13 +480,14 @@ hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {
     hipLaunchKernelGGL(hybrid_mask_kernel, dim3(a.Hkv, a.B), dim3(256), words * sizeof(uint32_t), stream, a);
   }
   const dim3 grid(a.n_split, a.Hkv, a.B);
+  const dim3 grid_bf(a.n_bf16 > 0 ? a.n_bf16 : 1, a.Hkv, a.B);
   if (D == 128) {
     hipLaunchKernelGGL(decode_fp4_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
-    if (a.hybrid) hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3(1, a.Hkv, a.B), dim3(kDecThreads), 0, stream, a);
+    if (a.hybrid && a.n_bf16 > 0) hipLaunchKernelGGL(decode_bf16_kernel<128>, grid_bf, dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.Hq, a.B), dim3(128), 0, stream, a);
   } else {
     hipLaunchKernelGGL(decode_fp4_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
-    if (a.hybrid) hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(1, a.Hkv, a.B), dim3(kDecThreads), 0, stream, a);
+    if (a.hybrid && a.n_bf16 > 0) hipLaunchKernelGGL(decode_bf16_kernel<64>, grid_bf, dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.Hq, a.B), dim3(64), 0, stream, a);
   }
   return hipGetLastError();

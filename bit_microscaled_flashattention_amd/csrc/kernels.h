@@ -64,7 +64,8 @@ struct DecodeArgs {
   float c;
   float softmax_scale;
   int split_len, n_split;
-  float* part;          // [B][Hq][n_split+1][D+2] partial (O, m, l)
+  int n_bf16;           // partial slots of the bf16 hybrid set (0 without hybrid)
+  float* part;          // [B][Hq][n_split+n_bf16][D+2] partial (O, m, l)
   float* out;
   float* lse;
   // hybrid

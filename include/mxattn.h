@@ -164,8 +164,9 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
  *            k_win/v_win [B][Hkv][window][D] (row w = token ctx-window+w);
  *            every other token uses the MXFP4 operands.  Each token counts
  *            once; one softmax covers all of them.
- *   split_len  tokens per split (multiple of 64); the splits are merged with
- *            their log-sum-exp in a fixed order (deterministic).
+ *   split_len  tokens per split (multiple of 64); the splits (and the bf16
+ *            set, in parts of 256 rows) are merged with their log-sum-exp in
+ *            a fixed order (deterministic); at most 4096 parts in total.
  *   workspace  device memory of mxattn_decode_workspace_bytes(...) bytes.
  *   out      fp32 [B][Hq][D];  lse nullable fp32 [B][Hq].
  * P is not quantised; logits and softmax state are fp32.
@@ -181,8 +182,10 @@ typedef struct {
   const void* v_win;
 } mxattn_hybrid_t;
 
+/* Workspace of mxattn_decode: hybrid_rows = max_sel + window of the hybrid
+ * set (0 without one).  Returns 0 for invalid sizes. */
 size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int64_t dim,
-                                     int64_t tcap, int32_t split_len, int32_t hybrid);
+                                     int64_t tcap, int32_t split_len, int32_t hybrid_rows);
 
 mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mxattn_mx_t* k_cache,
                               const mxattn_mx_t* v_cache, const int32_t* ctx_len,
