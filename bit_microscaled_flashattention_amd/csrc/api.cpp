@@ -139,8 +139,13 @@ mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int
   if ((st = check_mx(out, "quantize.out", -1)) != MXATTN_OK) return st;
   for (int i = 0; i < 3; ++i)
     if (x_stride[i] < 0) return fail(MXATTN_ERR_INVALID_ARG, "quantize: negative input stride");
+  // Rows are read 8 elements (16 or 32 bytes) at a time.
   const int esz = x_dtype == MXATTN_F32 ? 4 : 2;
-  if ((reinterpret_cast<uintptr_t>(x) % esz) != 0) return fail(MXATTN_ERR_INVALID_ARG, "quantize: misaligned input");
+  if ((reinterpret_cast<uintptr_t>(x) % 16) != 0 || (x_stride[0] * esz) % 16 != 0 || (x_stride[1] * esz) % 16 != 0 ||
+      (x_stride[2] * esz) % 16 != 0)
+    return fail(MXATTN_ERR_INVALID_ARG, "quantize: input and its row strides must be 16-byte aligned");
+  if (chan_scale != nullptr && (reinterpret_cast<uintptr_t>(chan_scale) % 16) != 0)
+    return fail(MXATTN_ERR_INVALID_ARG, "quantize: chan_scale must be 16-byte aligned");
   QuantArgs a{};
   a.x = x;
   a.dtype = x_dtype == MXATTN_F32 ? 0 : (x_dtype == MXATTN_F16 ? 1 : 2);
@@ -253,7 +258,6 @@ size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int
   const int64_t n_slot = (tcap + split_len - 1) / split_len + bf16_slots(hybrid_rows);
   size_t bytes = static_cast<size_t>(batch * hq * n_slot * (dim + 2)) * sizeof(float);
   bytes = (bytes + 255) / 256 * 256;
-  if (hybrid_rows > 0) bytes += static_cast<size_t>(batch * hkv * ((tcap + 31) / 32)) * sizeof(uint32_t);
   return bytes;
 }
 
@@ -277,7 +281,10 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
   if (split_len < 64 || split_len % 64 != 0) return fail(MXATTN_ERR_UNSUPPORTED, "decode: split_len must be a positive multiple of 64");
   if (!(softmax_scale >= 0.0f) || !std::isfinite(softmax_scale))
     return fail(MXATTN_ERR_INVALID_ARG, "decode: softmax_scale must be finite and >= 0");
-  if (kc->seq > 0x7FFFFFFF) return fail(MXATTN_ERR_UNSUPPORTED, "decode: cache too long");
+  // The scan addresses one (batch, KV head) of the cache with 32-bit offsets.
+  for (const mxattn_mx_t* c : {kc, vc})
+    if (c->seq * c->code_stride[2] > 0x7FFFFFFF || c->seq * c->scale_stride[2] > 0x7FFFFFFF)
+      return fail(MXATTN_ERR_UNSUPPORTED, "decode: one head of the cache must span less than 2 GiB");
   const int hybrid = hy != nullptr;
   if (hybrid) {
     if (q_bf16 == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid needs q_bf16");
@@ -285,7 +292,7 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
     if (hy->max_sel > 0 && (!hy->idx || !hy->n_sel || !hy->k_sel || !hy->v_sel))
       return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid selected set pointers missing");
     if (hy->window > 0 && (!hy->k_win || !hy->v_win)) return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid window pointers missing");
-    if (kc->seq > (1 << 19)) return fail(MXATTN_ERR_UNSUPPORTED, "decode: hybrid needs Tcap <= 524288");
+    if (split_len > 8192) return fail(MXATTN_ERR_UNSUPPORTED, "decode: hybrid needs split_len <= 8192");
     if (hy->max_sel + static_cast<int64_t>(hy->window) > kc->seq)
       return fail(MXATTN_ERR_INVALID_ARG, "decode: max_sel + window exceeds the cache");
   }
@@ -327,9 +334,6 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
     a.v_sel = static_cast<const uint16_t*>(hy->v_sel);
     a.k_win = static_cast<const uint16_t*>(hy->k_win);
     a.v_win = static_cast<const uint16_t*>(hy->v_win);
-    size_t part_bytes = static_cast<size_t>(a.B) * a.Hq * (a.n_split + a.n_bf16) * (q->dim + 2) * sizeof(float);
-    part_bytes = (part_bytes + 255) / 256 * 256;
-    a.mask = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + part_bytes);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return after_launch(launch_decode(a, static_cast<int>(q->dim), s), s, "decode");

@@ -208,14 +208,27 @@ __device__ __forceinline__ void stage_v(const ChunkRegs& r, uint8_t* vr, int lan
   }
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets past the end
+// return zero and fetch nothing, so tail and padding lanes need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past every buffer
+constexpr int kAuxStream = 2;                   // non-temporal: the cache is read once
+
+// Bitmap of the selected tokens of one split held in LDS (bit t - t_begin).
+constexpr int kMaxSplitWords = 8192 / 32;
+
 // FP4 cache scan of one split.  Each wave streams its own chunks (wave w
 // takes chunks w, w+4, ...) with two chunks of loads in flight, through its
 // own LDS staging rows, so the waves never wait for each other until the
-// final combine.
+// final combine.  Every load is unconditional (range-checked by the buffer
+// resource), which keeps the wait counts exact: the scan of one chunk waits
+// only for that chunk's bytes.
 template <int D>
-__global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, uint32_t* selbits, int split,
+                                          int hk, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.Hq / a.Hkv;
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a
   const int win = a.hybrid ? (a.window < ctx ? a.window : ctx) : 0;
   const int end4 = ctx - win;                    // 4-bit tokens are [0, end4)
   const int t_begin = split * a.split_len;
-  const int t_end = min(t_begin + a.split_len, end4);
+  const int t_end = max(t_begin, min(t_begin + a.split_len, end4));
 
   // Query operand: column j (query head hk*G + j), channels [32g, 32g+32).
   v4i qop = {0, 0, 0, 0};
@@ -236,11 +249,11 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a
     qop = *reinterpret_cast<const v4i*>(qc + g * 16);
     qsc = qs[g];
   }
-  const uint8_t* kc = a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1];
-  const uint8_t* ks = a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1];
-  const uint8_t* vc = a.v.codes + b * a.v.cs[0] + hk * a.v.cs[1];
-  const uint8_t* vs = a.v.scales + b * a.v.ss[0] + hk * a.v.ss[1];
-  const uint32_t* mask = a.hybrid ? a.mask + (static_cast<int64_t>(b) * a.Hkv + hk) * ((a.Tcap + 31) / 32) : nullptr;
+  const int64_t kcs = a.k.cs[2], kss = a.k.ss[2], vcs = a.v.cs[2], vss = a.v.ss[2];
+  const __amdgpu_buffer_rsrc_t rkc = make_rsrc(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], uint32_t(t_end * kcs));
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1], uint32_t(t_end * kss));
+  const __amdgpu_buffer_rsrc_t rvc = make_rsrc(a.v.codes + b * a.v.cs[0] + hk * a.v.cs[1], uint32_t(t_end * vcs));
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v.scales + b * a.v.ss[0] + hk * a.v.ss[1], uint32_t(t_end * vss));
   uint8_t* vr = vstage + wave * kChunk * kVRow;
 
   DecState st;
@@ -255,9 +268,10 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a
     for (int h = 0; h < 2; ++h) {
       const int t = t0 + h * 16 + j;
       const bool ok = t < t_end && g < nblk_d;
-      r.k[h] = ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(kc + static_cast<int64_t>(t) * a.k.cs[2] + g * 16))
-                  : v4i{0, 0, 0, 0};
-      r.ks[h] = ok ? ks[static_cast<int64_t>(t) * a.k.ss[2] + g] : 0;
+      const uint32_t oc = ok ? uint32_t(t * kcs + g * 16) : kOutOfRange;
+      const uint32_t os = ok ? uint32_t(t * kss + g) : kOutOfRange;
+      r.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rkc, oc, 0, kAuxStream);
+      r.ks[h] = __builtin_amdgcn_raw_buffer_load_b8(rks, os, 0, 0);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -265,17 +279,34 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a
       const int tt = bi / nblk_d, db = bi % nblk_d;
       const int t = t0 + tt;
       const bool ok = tt < kChunk && t < t_end;
-      r.v[h] = ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(vc + static_cast<int64_t>(t) * a.v.cs[2] + db * 16))
-                  : v4i{0, 0, 0, 0};
-      r.vs[h] = ok ? vs[static_cast<int64_t>(t) * a.v.ss[2] + db] : 127;
+      const uint32_t oc = ok ? uint32_t(t * vcs + db * 16) : kOutOfRange;
+      const uint32_t os = ok ? uint32_t(t * vss + db) : kOutOfRange;
+      r.v[h] = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 0, kAuxStream);
+      r.vs[h] = __builtin_amdgcn_raw_buffer_load_b8(rvs, os, 0, 0);
     }
   };
+
+  if (a.hybrid) {
+    // Selected tokens of this split (they are scored in the bf16 set).
+    const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
+    int nsel = a.max_sel > 0 ? a.n_sel[bh] : 0;
+    nsel = nsel < 0 ? 0 : (nsel > a.max_sel ? a.max_sel : nsel);
+    for (int w = threadIdx.x; w < kMaxSplitWords; w += kDecThreads) selbits[w] = 0u;
+    __syncthreads();
+    const int32_t* idx = a.idx + bh * a.max_sel;
+    for (int i = threadIdx.x; i < nsel; i += kDecThreads) {
+      const int t = idx[i];
+      if (t >= t_begin && t < t_end) atomicOr(&selbits[(t - t_begin) >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+  }
+
   auto process = [&](const ChunkRegs& r, int t0) {
     stage_v<D>(r, vr, lane);
     const v4f s0 = mfma16_fp4(r.k[0], qop, v4f{0, 0, 0, 0}, r.ks[0], qsc);
     const v4f s1 = mfma16_fp4(r.k[1], qop, v4f{0, 0, 0, 0}, r.ks[1], qsc);
     float sv[8];
-    const uint32_t mw = mask ? mask[t0 / 32] : 0u;   // chunks are 32-aligned
+    const uint32_t mw = a.hybrid ? selbits[(t0 - t_begin) >> 5] : 0u;   // chunks are 32-aligned
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tk = chunk_tok(g, i);
@@ -291,19 +322,25 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a
     pv_chunk(st, vr, lane, bhi, blo, alpha, moved, D);
   };
 
-  const int n_chunks = t_end > t_begin ? (t_end - t_begin + kChunk - 1) / kChunk : 0;
+  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
   const int mine = n_chunks > wave ? (n_chunks - wave + 3) / 4 : 0;   // chunks of this wave
   ChunkRegs A, B;
   auto chunk_t0 = [&](int i) { return t_begin + (wave + 4 * i) * kChunk; };
-  if (mine > 0) load(A, chunk_t0(0));
-  if (mine > 1) load(B, chunk_t0(1));
+  // The scheduling barriers keep each chunk's loads together and in issue
+  // order, so a chunk's wait never covers the loads of the chunk after it.
+  load(A, chunk_t0(0));
+  __builtin_amdgcn_sched_barrier(0);
+  load(B, chunk_t0(1));
+  __builtin_amdgcn_sched_barrier(0);
   for (int i = 0; i < mine; i += 2) {
     process(A, chunk_t0(i));
-    if (i + 2 < mine) load(A, chunk_t0(i + 2));
-    if (i + 1 < mine) {
-      process(B, chunk_t0(i + 1));
-      if (i + 3 < mine) load(B, chunk_t0(i + 3));
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    load(A, chunk_t0(i + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < mine) process(B, chunk_t0(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load(B, chunk_t0(i + 3));
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   combine_store<D>(vstage, st, a, b, hk, split, a.n_split + a.n_bf16);
@@ -311,12 +348,10 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_fp4_kernel(DecodeArgs a
 
 // ---------------------------------------------------------------------------
 // bf16 hybrid set: the selected rows (those below ctx - window) followed by
-// the window rows, kBf16Rows rows per workgroup (blockIdx.x), each result in
-// its own partial slot after the 4-bit splits.
+// the window rows, kBf16Rows rows per workgroup, each result in its own
+// partial slot after the 4-bit splits.
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
-  const int part_id = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, int part_id, int hk, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
   const int G = a.Hq / a.Hkv;
@@ -401,28 +436,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   combine_store<D>(vstage, st, a, b, hk, a.n_split + part_id, a.n_split + a.n_bf16);
 }
 
-// ---------------------------------------------------------------------------
-// Bitmap of the selected tokens that the bf16 set holds (idx < ctx-window),
-// one workgroup per (batch, KV head); built in LDS, written whole.
-__global__ __launch_bounds__(256) void hybrid_mask_kernel(DecodeArgs a) {
-  extern __shared__ uint32_t bits[];
-  const int hk = blockIdx.x, b = blockIdx.y;
-  const int words = (a.Tcap + 31) / 32;
-  const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
-  for (int w = threadIdx.x; w < words; w += blockDim.x) bits[w] = 0u;
-  __syncthreads();
-  int ctx = a.ctx_len[b];
-  ctx = ctx < 1 ? 1 : (ctx > a.Tcap ? a.Tcap : ctx);
-  const int win = a.window < ctx ? a.window : ctx;
-  int nsel = a.max_sel > 0 ? a.n_sel[bh] : 0;
-  nsel = nsel < 0 ? 0 : (nsel > a.max_sel ? a.max_sel : nsel);
-  for (int i = threadIdx.x; i < nsel; i += blockDim.x) {
-    const int t = a.idx[bh * a.max_sel + i];
-    if (t >= 0 && t < ctx - win) atomicOr(&bits[t >> 5], 1u << (t & 31));
-  }
-  __syncthreads();
-  uint32_t* dst = a.mask + bh * words;
-  for (int w = threadIdx.x; w < words; w += blockDim.x) dst[w] = bits[w];
+// One launch for the whole scan: blockIdx.x < n_split are the 4-bit splits,
+// the rest the bf16 hybrid parts, so the two kinds share the machine.
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 3) void decode_scan_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
+  __shared__ uint32_t selbits[kMaxSplitWords];
+  if (static_cast<int>(blockIdx.x) < a.n_split)
+    fp4_split<D>(a, vstage, selbits, blockIdx.x, blockIdx.y, blockIdx.z);
+  else
+    bf16_part<D>(a, vstage, blockIdx.x - a.n_split, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------
@@ -475,19 +498,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {
-  if (a.hybrid) {
-    const size_t words = (a.Tcap + 31) / 32;
-    hipLaunchKernelGGL(hybrid_mask_kernel, dim3(a.Hkv, a.B), dim3(256), words * sizeof(uint32_t), stream, a);
-  }
-  const dim3 grid(a.n_split, a.Hkv, a.B);
-  const dim3 grid_bf(a.n_bf16 > 0 ? a.n_bf16 : 1, a.Hkv, a.B);
+  const dim3 grid(a.n_split + (a.hybrid ? a.n_bf16 : 0), a.Hkv, a.B);
   if (D == 128) {
-    hipLaunchKernelGGL(decode_fp4_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
-    if (a.hybrid && a.n_bf16 > 0) hipLaunchKernelGGL(decode_bf16_kernel<128>, grid_bf, dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_scan_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.Hq, a.B), dim3(128), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_fp4_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
-    if (a.hybrid && a.n_bf16 > 0) hipLaunchKernelGGL(decode_bf16_kernel<64>, grid_bf, dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_scan_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.Hq, a.B), dim3(64), 0, stream, a);
   }
   return hipGetLastError();

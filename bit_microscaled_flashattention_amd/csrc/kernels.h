@@ -78,7 +78,6 @@ struct DecodeArgs {
   const uint16_t* v_sel;
   const uint16_t* k_win;
   const uint16_t* v_win;
-  uint32_t* mask;       // [B][Hkv][Tcap/32] bitmap of bf16-held tokens
 };
 
 struct SelectArgs {

@@ -114,29 +114,36 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int hk, 
                                      (__attribute__((address_space(3))) void*)(stage + C::OFF_V + i * 1024),
                                      16, 0, 0);
   }
+  // Scale bytes: indices are clamped instead of branched on; a clamped key
+  // is masked and a clamped V block only meets P = 0, and both read real
+  // (finite) scale bytes.
 #pragma unroll
   for (int i = 0; i < C::IKS; ++i) {
-    const int e = tid + kThreads * i;
-    uint8_t x = 0;
-    if (e < C::NKS) {
-      const int r = e / C::KSROW, part = e % C::KSROW;
-      const int t = t0 + (r & ~31) + sigma(r & 31);
-      if (t < a.Sk) x = ks[t * a.k.ss[2] + part];
-    }
-    sr.ks[i] = x;
+    const int e = (tid + kThreads * i) % C::NKS;
+    const int r = e / C::KSROW, part = e % C::KSROW;
+    int t = t0 + (r & ~31) + sigma(r & 31);
+    t = t < a.Sk ? t : a.Sk - 1;
+    sr.ks[i] = ks[t * a.k.ss[2] + part];
   }
 #pragma unroll
   for (int i = 0; i < C::IVS; ++i) {
-    const int e = tid + kThreads * i;
-    uint8_t x = 0;
-    if (e < C::NVS) {
-      const int d = e / C::VSROW, part = e % C::VSROW;
-      const int blk = t0 / 32 + part;
-      if (blk < nblk) x = vs[d * a.v.ss[2] + blk];
-    }
-    sr.vs[i] = x;
+    const int e = (tid + kThreads * i) % C::NVS;
+    const int d = e / C::VSROW, part = e % C::VSROW;
+    int blk = t0 / 32 + part;
+    blk = blk < nblk ? blk : nblk - 1;
+    sr.vs[i] = vs[d * a.v.ss[2] + blk];
   }
 }
+
+// The scale bytes of one LDS scale row (2, 4 or 8 bytes) as a 64-bit word.
+template <int ROWBYTES>
+__device__ __forceinline__ uint64_t scale_row(const uint8_t* base, int row) {
+  if constexpr (ROWBYTES == 8) return *reinterpret_cast<const uint64_t*>(base + row * 8);
+  if constexpr (ROWBYTES == 4) return *reinterpret_cast<const uint32_t*>(base + row * 4);
+  return *reinterpret_cast<const uint16_t*>(base + row * 2);
+}
+
+__device__ __forceinline__ int scale_byte(uint64_t w, int i) { return static_cast<int>((w >> (8 * i)) & 0xFF); }
 
 template <int D, int BC>
 __device__ __forceinline__ void store_scales(const ScaleRegs<D, BC>& sr, uint8_t* stage, int tid) {
@@ -246,18 +253,20 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
       const uint8_t* Ks = base + C::OFF_KS;
       const uint8_t* Vs = base + C::OFF_VS;
 
-      // ---- S^T = K_hat Q_hat^T
+      // ---- S^T = K_hat Q_hat^T (each block's operands are read into their
+      // own registers before its MFMAs, so LDS latency overlaps the MFMAs)
       v16f S[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const int r = kb * 32 + j;
+        v4i aop[C::DC];
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc)
+          aop[dc] = *reinterpret_cast<const v4i*>(Kc + r * C::KRB + 16 * swz<C::KRB>(r, 2 * dc + hh));
+        const uint64_t ksw = scale_row<C::KSROW>(Ks, r);
         v16f acc = v16f{};
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) {
-          const v4i aop = *reinterpret_cast<const v4i*>(Kc + r * C::KRB + 16 * swz<C::KRB>(r, 2 * dc + hh));
-          const int sa = Ks[r * C::KSROW + 2 * dc + hh];
-          acc = mfma32_fp4(aop, qop[dc], acc, sa, qsc[dc]);
-        }
+        for (int dc = 0; dc < C::DC; ++dc) acc = mfma32_fp4(aop[dc], qop[dc], acc, scale_byte(ksw, 2 * dc + hh), qsc[dc]);
         S[kb] = acc;
       }
 
@@ -344,13 +353,16 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
         const auto r1 = __builtin_amdgcn_permlane32_swap(code[2 * pp][1], code[2 * pp + 1][1], false, false);
         const v4i bop = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
         const int bsc = hh ? eb[2 * pp + 1] : eb[2 * pp];
+        v4i aop[C::DT];
+        int sa[C::DT];
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const int vrow = dt * 32 + j;
-          const v4i aop = *reinterpret_cast<const v4i*>(Vc + vrow * C::VRB + 16 * swz<C::VRB>(vrow, 2 * pp + hh));
-          const int sa = Vs[vrow * C::VSROW + 2 * pp + hh];
-          O[dt] = mfma32_fp4(aop, bop, O[dt], sa, bsc);
+          aop[dt] = *reinterpret_cast<const v4i*>(Vc + vrow * C::VRB + 16 * swz<C::VRB>(vrow, 2 * pp + hh));
+          sa[dt] = scale_byte(scale_row<C::VSROW>(Vs, vrow), 2 * pp + hh);
         }
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) O[dt] = mfma32_fp4(aop[dt], bop, O[dt], sa[dt], bsc);
         L = mfma16_fp4(ones, bop, L, a.one_scale, bsc);
       }
     }

@@ -14,9 +14,60 @@
 namespace mxattn {
 
 // ---------------------------------------------------------------------------
+// Eight consecutive elements of a row, widened to fp32, from one 16-byte
+// (16-bit types) or two 16-byte (fp32) loads.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t i, float* y) {
+  if constexpr (DT == 0) {
+    const v4f a = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(base) + i);
+    const v4f b = *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(base) + i + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[k] = a[k];
+      y[4 + k] = b[k];
+    }
+  } else {
+    const v4i w = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(base) + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t u = static_cast<uint32_t>(w[k]);
+      if constexpr (DT == 2) {
+        y[2 * k] = __uint_as_float(u << 16);
+        y[2 * k + 1] = __uint_as_float(u & 0xFFFF0000u);
+      } else {
+        y[2 * k] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xFFFFu)));
+        y[2 * k + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Head-dim blocks.  Four lanes own one 32-element block (8 elements each, one
 // 16-byte load for 16-bit inputs), so a wave covers 16 consecutive blocks and
 // every load and store is contiguous across the wave.
+// Eight elements to eight packed E2M1 codes (element i in nibble i) under
+// scale byte sb.  From byte 3 up the hardware convert does it: it rounds
+// y/2^e to nearest even on the E2M1 grid, saturates and keeps the sign, and
+// every fp32 subnormal element lands below 0.25 and codes to signed zero
+// whatever the convert's denormal handling.  Bytes 0..2 take the
+// integer-exact encoder.
+__device__ __forceinline__ uint32_t encode8(const float* y, int sb) {
+  uint32_t packed = 0;
+  if (sb >= 3) {
+    const float scl = scale_of_byte(sb);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], scl, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], scl, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], scl, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], scl, 3);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_code(y[i], sb) << (4 * i);
+  }
+  return packed;
+}
+
+template <int DT>
 __global__ __launch_bounds__(256) void quantize_hd_kernel(QuantArgs a) {
   const int64_t nblk_row = a.D / 32;
   const int64_t total = a.B * a.H * a.S * nblk_row;
@@ -34,15 +85,22 @@ __global__ __launch_bounds__(256) void quantize_hd_kernel(QuantArgs a) {
   const int64_t h = rest % a.H;
   const int64_t b = rest / a.H;
   const int64_t d0 = db * 32 + part * 8;
-  const int64_t xoff = b * a.xs[0] + h * a.xs[1] + s * a.xs[2] + d0;
 
   float y[8];
+  if (live) {
+    load8<DT>(a.x, b * a.xs[0] + h * a.xs[1] + s * a.xs[2] + d0, y);
+    if (a.chan_scale != nullptr) {
+      const v4f c0 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0);
+      const v4f c1 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0 + 4);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = live ? load_elem(a.x, xoff + i, a.dtype) : 0.0f;
-  if (a.chan_scale != nullptr && live) {
-    const float* cs = a.chan_scale + h * a.D + d0;
+      for (int k = 0; k < 4; ++k) {
+        y[k] = __fmul_rn(y[k], c0[k]);
+        y[4 + k] = __fmul_rn(y[4 + k], c1[k]);
+      }
+    }
+  } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(y[i], cs[i]);
+    for (int k = 0; k < 8; ++k) y[k] = 0.0f;
   }
   uint32_t amax = 0;
 #pragma unroll
@@ -55,9 +113,7 @@ __global__ __launch_bounds__(256) void quantize_hd_kernel(QuantArgs a) {
   uint32_t o2 = __shfl_xor(amax, 2, 4);
   amax = o2 > amax ? o2 : amax;
   const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
-  uint32_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= e2m1_code(y[i], sb) << (4 * i);
+  const uint32_t packed = encode8(y, sb);
   if (!live) return;
   uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + s * a.cs[2];
   *reinterpret_cast<uint32_t*>(crow + d0 / 2) = packed;
@@ -66,11 +122,12 @@ __global__ __launch_bounds__(256) void quantize_hd_kernel(QuantArgs a) {
 
 // ---------------------------------------------------------------------------
 // Sequence blocks (the key-blocked V layout of prefill).  A workgroup stages
-// 64 tokens x D channels in LDS as fp32, then each thread encodes one
-// (channel, 32-token block) and writes its 16 code bytes.  Tokens past S are
-// +0 padding inside the last block.
+// 64 tokens x D channels in LDS as fp32 (16-byte loads along the channels),
+// then each thread encodes one (channel, 32-token block) and writes its 16
+// code bytes.  Tokens past S are +0 padding inside the last block.
 constexpr int kKeyChunk = 64;
 
+template <int DT>
 __global__ __launch_bounds__(256) void quantize_key_kernel(QuantArgs a) {
   __shared__ float tile[kKeyChunk][129];
   const int64_t nchunk = (a.S + kKeyChunk - 1) / kKeyChunk;
@@ -80,15 +137,23 @@ __global__ __launch_bounds__(256) void quantize_key_kernel(QuantArgs a) {
   const int64_t b = bh / a.H;
   const int D = static_cast<int>(a.D);
   const int64_t t0 = chunk * kKeyChunk;
-  for (int i = threadIdx.x; i < kKeyChunk * D; i += blockDim.x) {
-    const int tt = i / D, d = i % D;
+  const int groups = D / 8;  // 8-channel groups per token
+  for (int i = threadIdx.x; i < kKeyChunk * groups; i += blockDim.x) {
+    const int tt = i / groups, d0 = (i % groups) * 8;
     const int64_t t = t0 + tt;
-    float y = 0.0f;
+    float y[8];
     if (t < a.S) {
-      y = load_elem(a.x, b * a.xs[0] + h * a.xs[1] + t * a.xs[2] + d, a.dtype);
-      if (a.chan_scale != nullptr) y = __fmul_rn(y, a.chan_scale[h * a.D + d]);
+      load8<DT>(a.x, b * a.xs[0] + h * a.xs[1] + t * a.xs[2] + d0, y);
+      if (a.chan_scale != nullptr) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(y[k], a.chan_scale[h * a.D + d0 + k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = 0.0f;
     }
-    tile[tt][d] = y;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tile[tt][d0 + k] = y[k];
   }
   __syncthreads();
   const int tasks = D * (kKeyChunk / 32);
@@ -103,8 +168,14 @@ __global__ __launch_bounds__(256) void quantize_key_kernel(QuantArgs a) {
       amax = m > amax ? m : amax;
     }
     const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
-    uint32_t w[4] = {0, 0, 0, 0};
-    for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_code(tile[sub * 32 + i][d], sb) << (4 * (i & 7));
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = tile[sub * 32 + q * 8 + i][d];
+      w[q] = encode8(y, sb);
+    }
     uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + static_cast<int64_t>(d) * a.cs[2];
     *reinterpret_cast<v4i*>(crow + tblk * 16) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     a.scales[b * a.ss[0] + h * a.ss[1] + static_cast<int64_t>(d) * a.ss[2] + tblk] = static_cast<uint8_t>(sb);
@@ -149,18 +220,23 @@ __global__ __launch_bounds__(256) void smooth_calibrate_kernel(CalibArgs a) {
   }
 }
 
-hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+template <int DT>
+static void launch_quantize_t(const QuantArgs& a, hipStream_t stream) {
   if (a.key_layout) {
     const int64_t nchunk = (a.S + kKeyChunk - 1) / kKeyChunk;
     const int64_t grid = nchunk * a.B * a.H;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_key_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+    if (grid > 0) hipLaunchKernelGGL(quantize_key_kernel<DT>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
   } else {
     const int64_t threads = a.B * a.H * a.S * (a.D / 32) * 4;
-    if (threads == 0) return hipSuccess;
     const int64_t grid = (threads + 255) / 256;
-    hipLaunchKernelGGL(quantize_hd_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+    if (grid > 0) hipLaunchKernelGGL(quantize_hd_kernel<DT>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
   }
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+  if (a.dtype == 0) launch_quantize_t<0>(a, stream);
+  else if (a.dtype == 1) launch_quantize_t<1>(a, stream);
+  else launch_quantize_t<2>(a, stream);
   return hipGetLastError();
 }
 

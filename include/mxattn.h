@@ -87,8 +87,9 @@ typedef struct {
  * FP4, "The KV Cache Bottleneck ..."; the optional per-channel factor is the
  * Smooth-QK rescale of HiFA4, Abstract).
  *   x          bf16/fp16/fp32 values; element (b,h,s,d) at
- *              x + (b*x_stride[0] + h*x_stride[1] + s*x_stride[2] + d) elements.
- *   chan_scale nullable; fp32 [H][D].  Each value is first widened to fp32 and
+ *              x + (b*x_stride[0] + h*x_stride[1] + s*x_stride[2] + d) elements;
+ *              x and every row start must be 16-byte aligned.
+ *   chan_scale nullable; fp32 [H][D], 16-byte aligned.  Each value is first widened to fp32 and
  *              multiplied by chan_scale[h][d] in IEEE fp32 (round to nearest
  *              even); the block maximum and codes are taken from that product.
  *   rule,qmax  the E8M0 rule (qmax is read for UOS only).
@@ -164,13 +165,15 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
  *            k_win/v_win [B][Hkv][window][D] (row w = token ctx-window+w);
  *            every other token uses the MXFP4 operands.  Each token counts
  *            once; one softmax covers all of them.
- *   split_len  tokens per split (multiple of 64); the splits (and the bf16
- *            set, in parts of 256 rows) are merged with their log-sum-exp in
- *            a fixed order (deterministic); at most 4096 parts in total.
+ *   split_len  tokens per split (multiple of 64; at most 8192 with a hybrid
+ *            set); the splits (and the bf16 set, in parts of 256 rows) are
+ *            merged with their log-sum-exp in a fixed order (deterministic);
+ *            at most 4096 parts in total.
  *   workspace  device memory of mxattn_decode_workspace_bytes(...) bytes.
  *   out      fp32 [B][Hq][D];  lse nullable fp32 [B][Hq].
  * P is not quantised; logits and softmax state are fp32.
- * Supported: D = 128 (D = 64 also), Hq/Hkv in {1,2,4,8}. */
+ * Supported: D = 128 (D = 64 also), Hq/Hkv in {1,2,4,8}; one (batch, KV
+ * head) of each cache spans less than 2 GiB (Tcap x row stride). */
 typedef struct {
   const int32_t* idx;   /* [B][Hkv][max_sel] */
   const int32_t* n_sel; /* [B][Hkv] */

@@ -125,7 +125,7 @@ def test_decode_workspace_and_rejects():
     n = mxa.decode_workspace_bytes(32, 32, 8, 128, 32768, 2048)
     assert n == 32 * 32 * 16 * 130 * 4
     nh = mxa.decode_workspace_bytes(8, 32, 8, 128, 32768, 2048, hybrid_rows=1632 + 128)
-    assert nh >= 8 * 32 * (16 + 7) * 130 * 4 + 8 * 8 * 1024 * 4
+    assert nh == 8 * 32 * (16 + 7) * 130 * 4
     assert mxa.decode_workspace_bytes(0, 32, 8, 128, 32768, 2048) == 0
     q = _mx(s=1, h=32); kc = _mx(s=32768, h=8); vc = _mx(s=32768, h=8)
     ctx = ctypes.c_void_p(64)
