@@ -30,6 +30,41 @@ PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline)"
 
+# HBM bytes per launch of the dominant kernels, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) each scaled by what the same
+# counter reads for an elementwise kernel of known size (--calibrate-copy).
+# A figure is reported only while the kernel's sources hash to the profiled
+# state; after any change to them it is null until profiled again.
+PROFILED_TRAFFIC = {
+    # fetch 7220 KiB x 2.000 + write 65607 KiB x 1.000 per dispatch
+    "prefill_kernel<128,128,true>": {"bytes": 81968323, "sources": "68aeba6ca671a0f1"},
+    # fetch 557414 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch
+    "decode_scan_kernel<128> split 4096": {"bytes": 1146007569, "sources": "585a6817441207fd"},
+}
+TRAFFIC_SOURCES = {
+    "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
+                "bit_microscaled_flashattention_amd/csrc/mx_device.h"],
+    "decode": ["bit_microscaled_flashattention_amd/csrc/decode.hip",
+               "bit_microscaled_flashattention_amd/csrc/mx_device.h"],
+}
+
+
+def sources_digest(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kind]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kind, key):
+    """Profiled HBM bytes per launch of `key`, or None if absent or stale."""
+    rec = PROFILED_TRAFFIC.get(key)
+    if rec is None or rec["sources"] != sources_digest(kind):
+        return None
+    return rec["bytes"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -42,6 +77,9 @@ def parse():
     ap.add_argument("--kv-tile", type=int, default=128)
     ap.add_argument("--decode-split", type=int, default=4096, help="tokens per split, 32K decode leg")
     ap.add_argument("--hybrid-split", type=int, default=2048, help="tokens per split, hybrid decode leg")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run an elementwise kernel of known size (1 GiB in, 1 GiB out) three times, "
+                         "to scale HBM byte counters; prints the source digests of the profiled kernels")
     return ap.parse_args()
 
 
@@ -199,14 +237,15 @@ def decode_leg(args, flush):
     alg = cache_bytes + B * HQ * (D // 2 + D // 32) + B * HQ * D * 4
     return {
         "workload": "batch 32, 32/8 heads, head_dim 128, ctx 32768, MXFP4 K/V cache (E2M1 + E8M0 per 32 "
-                    "along head_dim), MXFP4 query, split 2048; step = quantise q + decode (scan + merge)",
+                    f"along head_dim), MXFP4 query, split {SPLIT}; step = quantise q + decode (scan + merge)",
         "ms_per_token": round(t_step * 1e3, 4),
         "GB_per_s": round(alg / t_step / 1e9, 1),
         "algorithmic_bytes": alg,
         "roofline": {"bound": "hbm", "kernel": "mxattn_decode (decode_scan_kernel<128> + merge)",
                      "achieved": round(alg / t_call / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(alg / t_call / 1e9 / PEAK_HBM_GBS, 4),
-                     "call_ms": round(t_call * 1e3, 4), "traffic": None},
+                     "call_ms": round(t_call * 1e3, 4),
+                     "traffic": profiled_traffic("decode", f"decode_scan_kernel<128> split {SPLIT}")},
         "cache": "flushed (512 MB read of another buffer) before every timed step",
     }
 
@@ -283,6 +322,16 @@ def main():
               "(multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        x = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "torch.neg int32", "bytes_read": x.numel() * 4,
+                          "bytes_written": y.numel() * 4,
+                          "sources": {k: sources_digest(k) for k in TRAFFIC_SOURCES}}))
+        return
     legs = set(args.legs.split(","))
     pre, d, cal = prefill_leg(args)
     line = {
@@ -305,7 +354,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,128,causal>",
                      "achieved": round(pre["kernel_tflops"], 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre["kernel_tflops"] / PEAK_FP4_TFLOPS, 4),
-                     "kernel_ms": round(pre["kernel_s"] * 1e3, 4), "traffic": None},
+                     "kernel_ms": round(pre["kernel_s"] * 1e3, 4),
+                     "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,true>")},
     }
     del d
     torch.cuda.empty_cache()
