@@ -78,60 +78,87 @@ struct ScaleRegs {
   uint8_t vs[Cfg<D, BC>::IVS];
 };
 
+// Buffer resources over one (batch, KV head) of the K and V operands.  K
+// rows past the sequence lie past the K resources' end: their loads return
+// zeros without fetching (those keys are masked).  V rows are channels, so a
+// block index past the sequence is clamped to the last block instead (those
+// keys only meet P = 0).
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+  int kcs, kss, vcs, vss;  // row strides in bytes
+  int nblk;                // 32-key blocks of the sequence
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ TileSrc make_tile_src(const PrefillArgs& a, int b, int hk) {
+  TileSrc t;
+  t.kcs = static_cast<int>(a.k.cs[2]);
+  t.kss = static_cast<int>(a.k.ss[2]);
+  t.vcs = static_cast<int>(a.v.cs[2]);
+  t.vss = static_cast<int>(a.v.ss[2]);
+  t.nblk = (a.Sk + 31) / 32;
+  t.kc = rsrc_of(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], static_cast<int64_t>(a.Sk) * t.kcs);
+  t.ks = rsrc_of(a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1], static_cast<int64_t>(a.Sk) * t.kss);
+  t.vc = rsrc_of(a.v.codes + b * a.v.cs[0] + hk * a.v.cs[1], static_cast<int64_t>(D) * t.vcs);
+  t.vs = rsrc_of(a.v.scales + b * a.v.ss[0] + hk * a.v.ss[1], static_cast<int64_t>(D) * t.vss);
+  return t;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // Issue the direct HBM->LDS loads of a tile's K and V codes (this wave's
 // share of the 1 KB loads) and fetch its share of the scale bytes into
-// registers.  Rows past the sequence read a clamped valid row; their logits
-// are masked and their P is 0, so the bytes never matter.
+// registers.  `wave` is wave-uniform (a scalar), so the LDS destinations are
+// scalars and the trip counts static.  Whole offsets go in the per-lane
+// operand, which is what the resource's range check covers.  V code blocks past the sequence read whatever lies
+// next in the V resource (another channel's finite codes, or zeros past its
+// end): those keys only meet P = 0.  V scale blocks are clamped to the last
+// real block, so the scale applied to them is a real, finite one.
 template <int D, int BC>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int hk, int t0, uint8_t* stage,
-                                           ScaleRegs<D, BC>& sr, int tid) {
+__device__ __forceinline__ void issue_tile(const TileSrc& src, int t0, uint8_t* stage, ScaleRegs<D, BC>& sr,
+                                           int tid, int wave) {
   using C = Cfg<D, BC>;
-  const int wave = tid >> 6, lane = tid & 63;
-  const uint8_t* kc = a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1];
-  const uint8_t* ks = a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1];
-  const uint8_t* vc = a.v.codes + b * a.v.cs[0] + hk * a.v.cs[1];
-  const uint8_t* vs = a.v.scales + b * a.v.ss[0] + hk * a.v.ss[1];
-  const int nblk = (a.Sk + 31) / 32;
+  const int lane = tid & 63;
 #pragma unroll
-  for (int i = wave; i < C::K_LOADS; i += 4) {
+  for (int k = 0; k < (C::K_LOADS + 3) / 4; ++k) {
+    const int i = wave + 4 * k;
+    if (C::K_LOADS % 4 != 0 && i >= C::K_LOADS) break;
     const int o = i * 1024 + 16 * lane;
     const int r = o / C::KRB, pos = (o % C::KRB) / 16;
     const int chunk = pos ^ ((r / (256 / C::KRB)) % (C::KRB / 16));
-    int t = t0 + (r & ~31) + sigma(r & 31);
-    t = t < a.Sk ? t : a.Sk - 1;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kc + t * a.k.cs[2] + chunk * 16),
-                                     (__attribute__((address_space(3))) void*)(stage + i * 1024),
-                                     16, 0, 0);
+    const int rt = (r & ~31) + sigma(r & 31);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.kc, (lds_ptr_t)(stage + i * 1024), 16,
+                                             static_cast<uint32_t>((t0 + rt) * src.kcs + chunk * 16), 0, 0, 0);
   }
 #pragma unroll
-  for (int i = wave; i < C::V_LOADS; i += 4) {
+  for (int k = 0; k < (C::V_LOADS + 3) / 4; ++k) {
+    const int i = wave + 4 * k;
+    if (C::V_LOADS % 4 != 0 && i >= C::V_LOADS) break;
     const int o = i * 1024 + 16 * lane;
     const int d = o / C::VRB, pos = (o % C::VRB) / 16;
     const int chunk = pos ^ ((d / (256 / C::VRB)) % (C::VRB / 16));
-    int blk = t0 / 32 + chunk;
-    blk = blk < nblk ? blk : nblk - 1;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vc + d * a.v.cs[2] + blk * 16),
-                                     (__attribute__((address_space(3))) void*)(stage + C::OFF_V + i * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.vc, (lds_ptr_t)(stage + C::OFF_V + i * 1024), 16,
+                                             static_cast<uint32_t>(d * src.vcs + (t0 / 32 + chunk) * 16), 0, 0, 0);
   }
-  // Scale bytes: indices are clamped instead of branched on; a clamped key
-  // is masked and a clamped V block only meets P = 0, and both read real
-  // (finite) scale bytes.
 #pragma unroll
   for (int i = 0; i < C::IKS; ++i) {
     const int e = (tid + kThreads * i) % C::NKS;
     const int r = e / C::KSROW, part = e % C::KSROW;
-    int t = t0 + (r & ~31) + sigma(r & 31);
-    t = t < a.Sk ? t : a.Sk - 1;
-    sr.ks[i] = ks[t * a.k.ss[2] + part];
+    const int rt = (r & ~31) + sigma(r & 31);
+    sr.ks[i] = __builtin_amdgcn_raw_buffer_load_b8(src.ks, static_cast<uint32_t>((t0 + rt) * src.kss + part), 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::IVS; ++i) {
     const int e = (tid + kThreads * i) % C::NVS;
     const int d = e / C::VSROW, part = e % C::VSROW;
     int blk = t0 / 32 + part;
-    blk = blk < nblk ? blk : nblk - 1;
-    sr.vs[i] = vs[d * a.v.ss[2] + blk];
+    blk = blk < src.nblk ? blk : src.nblk - 1;
+    sr.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(src.vs, static_cast<uint32_t>(d * src.vss + blk), 0, 0);
   }
 }
 
@@ -158,6 +185,17 @@ __device__ __forceinline__ void store_scales(const ScaleRegs<D, BC>& sr, uint8_t
     const int e = tid + kThreads * i;
     if (e < C::NVS) stage[C::OFF_VS + e] = sr.vs[i];
   }
+}
+
+// E8M0 byte of a P block maximum pmax in [0, 1]: floor(log2 pmax) - 2 (OCP),
+// one more when the significand exceeds thr (UOS), clamped below at 1 so the
+// convert's scale stays a normal float (zero and tiny maxima take byte 1;
+// their codes are 0 either way).  pmax <= 1 keeps the byte below 126.
+__device__ __forceinline__ int p_scale_byte(float pmax, int thr) {
+  const uint32_t bits = __float_as_uint(pmax);
+  const int inc = static_cast<int>(bits & 0x7FFFFFu) > thr ? 1 : 0;
+  const int b = static_cast<int>(bits >> 23) - 2 + inc;
+  return b < 1 ? 1 : b;
 }
 
 // Workgroup -> (query block, batch, query head).  Consecutive workgroups go
@@ -188,17 +226,18 @@ __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int
 }
 
 template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, BC>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, j = lane & 31, hh = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   int qb, b, hq;
   map_block(a, CAUSAL, qb, b, hq);
   const int hk = hq / (a.Hq / a.Hkv);
   const int q0 = qb * kBR;
-  const int my_q = q0 + wave * 32 + j;
+  const int my_q = q0 + wave_s * 32 + j;
   const int qrow = my_q < a.Sq ? my_q : a.Sq - 1;  // padding rows recompute the last row
 
   // B operand of S^T: query qrow, channels [64 dc + 32 hh, +32).
@@ -216,9 +255,12 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
 
   const int last_q = (q0 + kBR - 1 < a.Sq - 1) ? q0 + kBR - 1 : a.Sq - 1;
   const int nt = CAUSAL ? last_q / BC + 1 : (a.Sk + BC - 1) / BC;
-  const int wave_last_q = (q0 + wave * 32 + 31 < a.Sq - 1) ? q0 + wave * 32 + 31 : a.Sq - 1;
+  const int wave_last_q = (q0 + wave_s * 32 + 31 < a.Sq - 1) ? q0 + wave_s * 32 + 31 : a.Sq - 1;
   const int my_nt = CAUSAL ? wave_last_q / BC + 1 : nt;
-  const int wave_first_q = q0 + wave * 32;
+  const int wave_first_q = q0 + wave_s * 32;
+  // Smallest and largest query row of this wave (padding rows repeat Sq - 1).
+  const int lo_q = wave_first_q < a.Sq - 1 ? wave_first_q : a.Sq - 1;
+  const int hi_q = wave_last_q;
 
   // E2M1 ones for the normaliser: a 16x16x128 A operand whose rows 0-7 sum
   // the k-groups of lanes 0-15 and 32-47 (queries 0-15 of both key blocks)
@@ -229,6 +271,19 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   const v4i ones = {onev, onev, onev, onev};
   const int l_query = (lane & 15) + 16 * (lane >> 5);
 
+  // Per-lane LDS byte offsets inside a stage.  The XOR swizzle of a row
+  // depends only on the row's position within its 32-row group, so key block
+  // kb / channel tile dt add the compile-time offsets kb*32*KRB / dt*32*VRB.
+  int koff[C::DC], voff[C::KB / 2];
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) koff[dc] = j * C::KRB + 16 * swz<C::KRB>(j, 2 * dc + hh);
+#pragma unroll
+  for (int pp = 0; pp < C::KB / 2; ++pp) voff[pp] = C::OFF_V + j * C::VRB + 16 * swz<C::VRB>(j, 2 * pp + hh);
+  const int ksoff = C::OFF_KS + j * C::KSROW, vsoff = C::OFF_VS + j * C::VSROW;
+  // UOS threshold on the significand bits of a P block maximum (never met
+  // under the OCP rule): significand 1.m above qmax/4, qmax/4 in (1, 2).
+  const int p_thr = a.p_uos ? static_cast<int>(__float_as_uint(a.p_qmax_quarter) & 0x7FFFFFu) : 0x7FFFFFFF;
+
   float m = -__builtin_huge_valf();
   float lsum = 0.0f;  // baseline normaliser (sum of unquantised P~)
   v16f O[C::DT];
@@ -236,8 +291,9 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   for (int dt = 0; dt < C::DT; ++dt) O[dt] = v16f{};
   v4f L = v4f{0, 0, 0, 0};
 
+  const TileSrc src = make_tile_src<D>(a, b, hk);
   ScaleRegs<D, BC> sr;
-  issue_tile<D, BC>(a, b, hk, 0, smem, sr, tid);
+  issue_tile<D, BC>(src, 0, smem, sr, tid, wave_s);
   store_scales<D, BC>(sr, smem, tid);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -245,53 +301,57 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   for (int jt = 0; jt < nt; ++jt) {
     const int t0 = jt * BC;
     uint8_t* next = smem + ((jt + 1) & 1) * C::STAGE;
-    if (jt + 1 < nt) issue_tile<D, BC>(a, b, hk, t0 + BC, next, sr, tid);
+    if (jt + 1 < nt) issue_tile<D, BC>(src, t0 + BC, next, sr, tid, wave_s);
     if (jt < my_nt) {
       const uint8_t* base = smem + (jt & 1) * C::STAGE;
-      const uint8_t* Kc = base;
-      const uint8_t* Vc = base + C::OFF_V;
-      const uint8_t* Ks = base + C::OFF_KS;
-      const uint8_t* Vs = base + C::OFF_VS;
 
-      // ---- S^T = K_hat Q_hat^T (each block's operands are read into their
-      // own registers before its MFMAs, so LDS latency overlaps the MFMAs)
-      v16f S[C::KB];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const int r = kb * 32 + j;
+      // Key block kb of this tile is [tb, tb + 32), tb = t0 + 32 kb.  Against
+      // this wave's 32 query rows it is fully visible, empty (skipped) or
+      // needs the per-element mask (the diagonal block, or keys past Sk).
+      auto blk_empty = [&](int kb) {
+        const int tb = t0 + kb * 32;
+        return tb >= a.Sk || (CAUSAL && tb > hi_q);
+      };
+      auto blk_masked = [&](int kb) {
+        const int tb = t0 + kb * 32;
+        return tb + 32 > a.Sk || (CAUSAL && tb + 31 > lo_q);
+      };
+      // Logits of block kb: S^T = K_hat Q_hat^T over the D/64 chunks.
+      auto logits = [&](int kb) -> v16f {
         v4i aop[C::DC];
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
-          aop[dc] = *reinterpret_cast<const v4i*>(Kc + r * C::KRB + 16 * swz<C::KRB>(r, 2 * dc + hh));
-        const uint64_t ksw = scale_row<C::KSROW>(Ks, r);
+          aop[dc] = *reinterpret_cast<const v4i*>(base + koff[dc] + kb * 32 * C::KRB);
+        const uint64_t ksw = scale_row<C::KSROW>(base + ksoff + kb * 32 * C::KSROW, 0);
         v16f acc = v16f{};
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) acc = mfma32_fp4(aop[dc], qop[dc], acc, scale_byte(ksw, 2 * dc + hh), qsc[dc]);
-        S[kb] = acc;
-      }
-
-      // ---- masks: causal (key > query) and keys past the end
-      const bool tail = t0 + BC > a.Sk;
-      const bool diag = CAUSAL && (t0 + BC - 1 > wave_first_q);
-      if (tail || diag) {
-        const int qlim = CAUSAL ? qrow : 0x7FFFFFFF;
+        if (blk_masked(kb)) {
+          const int qlim = CAUSAL ? qrow : 0x7FFFFFFF;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int t = t0 + kb * 32 + 16 * hh + r;
-            if (t > qlim || t >= a.Sk) S[kb][r] = -__builtin_huge_valf();
+          for (int r2 = 0; r2 < 16; ++r2) {
+            const int t = t0 + kb * 32 + 16 * hh + r2;
+            if (t > qlim || t >= a.Sk) acc[r2] = -__builtin_huge_valf();
           }
-      }
+        }
+        return acc;
+      };
 
-      // ---- block maxima (raw logits), running maximum
+      // ---- pass 1: block maxima of the raw logits, running maximum.  The
+      // logits are not kept: pass 2 recomputes them on the (otherwise idle)
+      // matrix cores, which keeps the register footprint at three waves per
+      // SIMD.
       float bm[C::KB];
       float tmax = -__builtin_huge_valf();
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        float x = S[kb][0];
+        bm[kb] = -__builtin_huge_valf();
+        if (blk_empty(kb)) continue;
+        const v16f S = logits(kb);
+        float x = __builtin_fmaxf(__builtin_fmaxf(S[0], S[1]), S[2]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) x = fmaxf(x, S[kb][r]);
+        for (int r = 3; r < 15; r += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, S[r]), S[r + 1]);
+        x = __builtin_fmaxf(x, S[15]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         bm[kb] = x;
@@ -301,41 +361,6 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
       const float alpha = fast_exp2((m - m_new) * a.c);
       const float mc = m_new * a.c;
 
-      // ---- P~ (in place of S), its MXFP4 codes, the PV B operands
-      uint32_t code[C::KB][2];
-      int eb[C::KB];
-      float tile_sum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const float pmax = fast_exp2((bm[kb] - m_new) * a.c);
-        int byte = e8m0_byte(__float_as_uint(pmax), a.p_uos != 0, a.p_qmax_quarter);
-        byte = byte < 1 ? 1 : byte;  // keep the convert's scale a normal float
-        eb[kb] = byte;
-        const float scl = scale_of_byte(byte);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb][r] = fast_exp2(__builtin_fmaf(S[kb][r], a.c, -mc));
-        if (!a.l_from_quantized) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tile_sum += S[kb][r];
-        }
-        const v16f& p = S[kb];
-        uint32_t w0 = 0, w1 = 0;
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[0], p[1], scl, 0);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[4], p[5], scl, 2);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[6], p[7], scl, 3);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[8], p[9], scl, 0);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[10], p[11], scl, 1);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[12], p[13], scl, 2);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[14], p[15], scl, 3);
-        code[kb][0] = w0;
-        code[kb][1] = w1;
-      }
-      if (!a.l_from_quantized) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tile_sum), __float_as_uint(tile_sum), false, false);
-        lsum = alpha * lsum + (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
-      }
-
       // ---- rescale the accumulators (skipped when no row's maximum moved)
       if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
 #pragma unroll
@@ -343,23 +368,58 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
         // L[0] of this lane is the normaliser of query l%16 + 16*(l/32),
         // whose factor lives in that query's lane.
         L[0] *= __shfl(alpha, l_query);
+        if (!a.l_from_quantized) lsum *= alpha;
       }
       m = m_new;
 
-      // ---- O^T += V_hat^T P_hat^T, and l += ones^T P_hat^T
+      // ---- pass 2, per pair of key blocks: logits again, P~ in place, its
+      // MXFP4 codes, then O^T += V_hat^T P_hat^T and l += ones^T P_hat^T.
 #pragma unroll
       for (int pp = 0; pp < C::KB / 2; ++pp) {
-        const auto r0 = __builtin_amdgcn_permlane32_swap(code[2 * pp][0], code[2 * pp + 1][0], false, false);
-        const auto r1 = __builtin_amdgcn_permlane32_swap(code[2 * pp][1], code[2 * pp + 1][1], false, false);
+        uint32_t code[2][2];
+        int eb[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int kb = 2 * pp + h2;
+          code[h2][0] = code[h2][1] = 0u;
+          eb[h2] = 1;
+          if (blk_empty(kb)) continue;
+          v16f p = logits(kb);
+          const int byte = p_scale_byte(fast_exp2((bm[kb] - m_new) * a.c), p_thr);
+          eb[h2] = byte;
+          const float scl = scale_of_byte(byte);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(p[r], a.c, -mc));
+          if (!a.l_from_quantized) {
+            float ts = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ts += p[r];
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts), __float_as_uint(ts), false, false);
+            lsum += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          }
+          uint32_t w0 = 0, w1 = 0;
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[0], p[1], scl, 0);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[4], p[5], scl, 2);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[6], p[7], scl, 3);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[8], p[9], scl, 0);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[10], p[11], scl, 1);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[12], p[13], scl, 2);
+          w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[14], p[15], scl, 3);
+          code[h2][0] = w0;
+          code[h2][1] = w1;
+        }
+        if (blk_empty(2 * pp) && blk_empty(2 * pp + 1)) continue;
+        const auto r0 = __builtin_amdgcn_permlane32_swap(code[0][0], code[1][0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(code[0][1], code[1][1], false, false);
         const v4i bop = {(int)r0[0], (int)r1[0], (int)r0[1], (int)r1[1]};
-        const int bsc = hh ? eb[2 * pp + 1] : eb[2 * pp];
+        const int bsc = hh ? eb[1] : eb[0];
         v4i aop[C::DT];
         int sa[C::DT];
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const int vrow = dt * 32 + j;
-          aop[dt] = *reinterpret_cast<const v4i*>(Vc + vrow * C::VRB + 16 * swz<C::VRB>(vrow, 2 * pp + hh));
-          sa[dt] = scale_byte(scale_row<C::VSROW>(Vs, vrow), 2 * pp + hh);
+          aop[dt] = *reinterpret_cast<const v4i*>(base + voff[pp] + dt * 32 * C::VRB);
+          sa[dt] = scale_byte(scale_row<C::VSROW>(base + vsoff + dt * 32 * C::VSROW, 0), 2 * pp + hh);
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) O[dt] = mfma32_fp4(aop[dt], bop, O[dt], sa[dt], bsc);
