@@ -18,7 +18,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxattn.so")
+# MXATTN_LIBRARY selects another build of the library (same ABI).
+LIB_PATH = os.environ.get("MXATTN_LIBRARY") or os.path.join(_HERE, "libmxattn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, F16, BF16 = 0, 1, 2

@@ -29,6 +29,8 @@
 //   * K/V tiles are double-buffered in LDS (rows padded to avoid bank
 //     conflicts); the grid is ordered longest-first for causal masks and
 //     mapped so that each XCD works on whole KV heads.
+#include <type_traits>
+
 #include "mx_device.h"
 #include "kernels.h"
 
@@ -225,8 +227,8 @@ __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int
   hq = (pair % a.Hkv) * G + g;
 }
 
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(PrefillArgs a) {
+template <int D, int BC, bool CAUSAL, bool LQ>
+__global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, BC>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
   const int tid = threadIdx.x;
@@ -298,23 +300,34 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int jt = 0; jt < nt; ++jt) {
+  // One tile step (prefetch the next tile, this tile's body, hand over the
+  // stage), compiled twice: FULL, for the leading tiles whose key blocks are
+  // all visible to every row of the workgroup (no per-block tests or
+  // branches), and the general form for the rest (the diagonal and tail
+  // tiles).  The two run as consecutive loops.  In the FULL form a
+  // scheduling barrier closes each block's work so the scheduler cannot
+  // hoist all blocks at once.
+  auto step = [&](const int jt, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int t0 = jt * BC;
     uint8_t* next = smem + ((jt + 1) & 1) * C::STAGE;
     if (jt + 1 < nt) issue_tile<D, BC>(src, t0 + BC, next, sr, tid, wave_s);
-    if (jt < my_nt) {
+    auto tile = [&]() {
       const uint8_t* base = smem + (jt & 1) * C::STAGE;
+      auto region_end = [&]() {
+        if constexpr (FULL) __builtin_amdgcn_sched_barrier(0);
+      };
 
       // Key block kb of this tile is [tb, tb + 32), tb = t0 + 32 kb.  Against
       // this wave's 32 query rows it is fully visible, empty (skipped) or
       // needs the per-element mask (the diagonal block, or keys past Sk).
       auto blk_empty = [&](int kb) {
         const int tb = t0 + kb * 32;
-        return tb >= a.Sk || (CAUSAL && tb > hi_q);
+        return !FULL && (tb >= a.Sk || (CAUSAL && tb > hi_q));
       };
       auto blk_masked = [&](int kb) {
         const int tb = t0 + kb * 32;
-        return tb + 32 > a.Sk || (CAUSAL && tb + 31 > lo_q);
+        return !FULL && (tb + 32 > a.Sk || (CAUSAL && tb + 31 > lo_q));
       };
       // Logits of block kb: S^T = K_hat Q_hat^T over the D/64 chunks.
       auto logits = [&](int kb) -> v16f {
@@ -337,25 +350,27 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
         return acc;
       };
 
-      // ---- pass 1: block maxima of the raw logits, running maximum.  The
-      // logits are not kept: pass 2 recomputes them on the (otherwise idle)
-      // matrix cores, which keeps the register footprint at three waves per
-      // SIMD.
+      // ---- logits of the tile, their block maxima, the running maximum.
+      // The logits stay in registers (64 per lane) for the exponentials.
+      v16f S[C::KB];
       float bm[C::KB];
       float tmax = -__builtin_huge_valf();
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         bm[kb] = -__builtin_huge_valf();
         if (blk_empty(kb)) continue;
-        const v16f S = logits(kb);
-        float x = __builtin_fmaxf(__builtin_fmaxf(S[0], S[1]), S[2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, S[r]), S[r + 1]);
-        x = __builtin_fmaxf(x, S[15]);
+        S[kb] = logits(kb);
+        const v16f& x16 = S[kb];
+        // Max of the 16 values as a depth-3 tree of max3 (no serial chain).
+        const float m0 = fmaxf(fmaxf(x16[0], x16[1]), x16[2]), m1 = fmaxf(fmaxf(x16[3], x16[4]), x16[5]);
+        const float m2 = fmaxf(fmaxf(x16[6], x16[7]), x16[8]), m3 = fmaxf(fmaxf(x16[9], x16[10]), x16[11]);
+        const float m4 = fmaxf(fmaxf(x16[12], x16[13]), x16[14]);
+        float x = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x16[15]));
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         bm[kb] = x;
         tmax = fmaxf(tmax, x);
+        region_end();
       }
       const float m_new = fmaxf(m, tmax);
       const float alpha = fast_exp2((m - m_new) * a.c);
@@ -368,12 +383,12 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
         // L[0] of this lane is the normaliser of query l%16 + 16*(l/32),
         // whose factor lives in that query's lane.
         L[0] *= __shfl(alpha, l_query);
-        if (!a.l_from_quantized) lsum *= alpha;
+        if (!LQ) lsum *= alpha;
       }
       m = m_new;
 
-      // ---- pass 2, per pair of key blocks: logits again, P~ in place, its
-      // MXFP4 codes, then O^T += V_hat^T P_hat^T and l += ones^T P_hat^T.
+      // ---- per pair of key blocks: P~ in place of the logits, its MXFP4
+      // codes, then O^T += V_hat^T P_hat^T and l += ones^T P_hat^T.
 #pragma unroll
       for (int pp = 0; pp < C::KB / 2; ++pp) {
         uint32_t code[2][2];
@@ -384,13 +399,13 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
           code[h2][0] = code[h2][1] = 0u;
           eb[h2] = 1;
           if (blk_empty(kb)) continue;
-          v16f p = logits(kb);
+          v16f& p = S[kb];
           const int byte = p_scale_byte(fast_exp2((bm[kb] - m_new) * a.c), p_thr);
           eb[h2] = byte;
           const float scl = scale_of_byte(byte);
 #pragma unroll
           for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(p[r], a.c, -mc));
-          if (!a.l_from_quantized) {
+          if constexpr (!LQ) {
             float ts = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) ts += p[r];
@@ -399,15 +414,16 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
           }
           uint32_t w0 = 0, w1 = 0;
           w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[0], p[1], scl, 0);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[4], p[5], scl, 2);
-          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[6], p[7], scl, 3);
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[8], p[9], scl, 0);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[10], p[11], scl, 1);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[4], p[5], scl, 2);
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[12], p[13], scl, 2);
+          w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[6], p[7], scl, 3);
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[14], p[15], scl, 3);
           code[h2][0] = w0;
           code[h2][1] = w1;
+          region_end();
         }
         if (blk_empty(2 * pp) && blk_empty(2 * pp + 1)) continue;
         const auto r0 = __builtin_amdgcn_permlane32_swap(code[0][0], code[1][0], false, false);
@@ -424,18 +440,27 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) O[dt] = mfma32_fp4(aop[dt], bop, O[dt], sa[dt], bsc);
         L = mfma16_fp4(ones, bop, L, a.one_scale, bsc);
+        region_end();
       }
-    }
+    };
+    if (FULL || jt < my_nt) tile();
     if (jt + 1 < nt) store_scales<D, BC>(sr, next, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
+  // Leading tiles fully visible to every row of the workgroup: keys below
+  // the first query row (causal) and below Sk.
+  const int full_keys = CAUSAL ? (q0 + 1 < a.Sk ? q0 + 1 : a.Sk) : a.Sk;
+  const int n_full = full_keys / BC < nt ? full_keys / BC : nt;
+  int jt = 0;
+  for (; jt < n_full; ++jt) step(jt, std::true_type{});
+  for (; jt < nt; ++jt) step(jt, std::false_type{});
 
   // ---- finalise: out = O / l, lse = m * softmax_scale + ln l
   // The normaliser of query j sits in lane j (j < 16) or j + 16 (j >= 16).
   const float lq = __shfl(L[0], j < 16 ? j : j + 16);
   if (my_q >= a.Sq) return;
-  const float l = a.l_from_quantized ? lq : lsum;
+  const float l = LQ ? lq : lsum;
   const float inv = 1.0f / l;
   const int64_t orow = (static_cast<int64_t>(b) * a.Hq + hq) * a.Sq + my_q;
   if (a.lse != nullptr && hh == 0) a.lse[orow] = m * a.softmax_scale + logf(l);
@@ -467,10 +492,15 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 2 : 3)) void prefill_kernel(
 template <int D, int BC>
 static void launch_t(const PrefillArgs& a, int causal, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.n_qblk) * a.B * a.Hq;
-  if (causal)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  const bool lq = a.l_from_quantized != 0;
+  if (causal && lq)
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (causal)
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (lq)
+    hipLaunchKernelGGL((prefill_kernel<D, BC, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BC, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream) {
