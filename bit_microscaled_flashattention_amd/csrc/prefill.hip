@@ -304,9 +304,7 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   // stage), compiled twice: FULL, for the leading tiles whose key blocks are
   // all visible to every row of the workgroup (no per-block tests or
   // branches), and the general form for the rest (the diagonal and tail
-  // tiles).  The two run as consecutive loops.  In the FULL form a
-  // scheduling barrier closes each block's work so the scheduler cannot
-  // hoist all blocks at once.
+  // tiles).  The two run as consecutive loops.
   auto step = [&](const int jt, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int t0 = jt * BC;
@@ -314,9 +312,6 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
     if (jt + 1 < nt) issue_tile<D, BC>(src, t0 + BC, next, sr, tid, wave_s);
     auto tile = [&]() {
       const uint8_t* base = smem + (jt & 1) * C::STAGE;
-      auto region_end = [&]() {
-        if constexpr (FULL) __builtin_amdgcn_sched_barrier(0);
-      };
 
       // Key block kb of this tile is [tb, tb + 32), tb = t0 + 32 kb.  Against
       // this wave's 32 query rows it is fully visible, empty (skipped) or
@@ -370,7 +365,6 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
         x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         bm[kb] = x;
         tmax = fmaxf(tmax, x);
-        region_end();
       }
       const float m_new = fmaxf(m, tmax);
       const float alpha = fast_exp2((m - m_new) * a.c);
@@ -423,7 +417,6 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[14], p[15], scl, 3);
           code[h2][0] = w0;
           code[h2][1] = w1;
-          region_end();
         }
         if (blk_empty(2 * pp) && blk_empty(2 * pp + 1)) continue;
         const auto r0 = __builtin_amdgcn_permlane32_swap(code[0][0], code[1][0], false, false);
@@ -440,7 +433,6 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) O[dt] = mfma32_fp4(aop[dt], bop, O[dt], sa[dt], bsc);
         L = mfma16_fp4(ones, bop, L, a.one_scale, bsc);
-        region_end();
       }
     };
     if (FULL || jt < my_nt) tile();
