@@ -370,6 +370,8 @@ mxattn_status_t mxattn_select_vertical(const mxattn_mx_t* q, const mxattn_mx_t* 
       return fail(MXATTN_ERR_UNSUPPORTED, "select: recent queries x group size above 512");
   }
   if (kc->seq > 65536) return fail(MXATTN_ERR_UNSUPPORTED, "select: cache longer than 65536");
+  if (kc->seq * kc->code_stride[2] > 0x7FFFFFFF || kc->seq * kc->scale_stride[2] > 0x7FFFFFFF)
+    return fail(MXATTN_ERR_UNSUPPORTED, "select: one head of the cache must span less than 2 GiB");
   const int64_t worst = kc->seq > window ? ((kc->seq - window) * rho_num + rho_den - 1) / rho_den : 0;
   if (worst > max_sel) return fail(MXATTN_ERR_INVALID_ARG, "select: max_sel %d below the worst-case count %lld", max_sel, (long long)worst);
   const size_t need = mxattn_select_workspace_bytes(kc->batch, q ? q->heads : kc->heads, R, kc->seq);

@@ -6,18 +6,21 @@
 // every 64 tokens.
 //
 // Kernels
-//   stats    -- per (context chunk, 128 recent queries): partial row max and
-//               row sum of the logits (S^T = K_hat q_hat^T on the scaled FP4
-//               MFMA), merged per query in chunk order by `finalize`.
-//   colmass  -- per 256-key block: the normalised probabilities of every
+//   stats    -- per (2048-key context chunk, batch x KV head): every recent
+//               query's partial row max and row sum of the logits (S^T =
+//               K_hat q_hat^T on the scaled FP4 MFMA, queries staged in
+//               LDS), merged per query in chunk order by `finalize`.
+//   colmass  -- per 512-key block: the normalised probabilities of every
 //               recent query of the KV head's group, summed per key (in-lane
 //               over 16 queries, a permlane32 swap for the other 16) and added
 //               to col_mass.  Each key belongs to exactly one lane: no atomics.
-//   topk     -- per (batch, KV head): exact radix select of the k-th largest
-//               mass (4 passes of 8 bits over the fp32 bit patterns, which
-//               order like the non-negative values), then one ordered
-//               compaction that emits the indices ascending, ties at the
-//               threshold going to the lower indices.
+//   topk     -- per (batch, KV head), one 1024-thread workgroup holding the
+//               masses in registers: the k-th largest fp32 bit pattern found
+//               bit by bit (bit patterns of non-negative values order like the
+//               values), then one ordered compaction that emits the indices
+//               ascending, ties at the threshold going to the lower indices.
+#include <type_traits>
+
 #include "mx_device.h"
 #include "kernels.h"
 
@@ -53,60 +56,159 @@ __device__ __forceinline__ float* stat_slot(const SelectArgs& a, int b, int hk, 
 }
 
 // ---------------------------------------------------------------------------
+constexpr int kMaxRecent = 512;    // recent queries x group size held in LDS
+
+// The group's recent queries in LDS: codes [nq][D/2] and scales [nq][D/32].
+// Queries past nq up to the next multiple of 32 are zero codes with scale
+// byte 0, so a whole group of 32 can be read without guards (their logits
+// are 0 and they are never reported).
 template <int D>
-__global__ __launch_bounds__(kSelThreads) void select_stats_kernel(SelectArgs a) {
-  const int chunk = blockIdx.x, qgrp = blockIdx.y, bh = blockIdx.z;
+__device__ __forceinline__ void stage_queries(const SelectArgs& a, int b, int hk, uint8_t* q_lds, uint8_t* qs_lds) {
+  const int G = a.Hq / a.Hkv;
+  const int nq = G * a.R, nq32 = (nq + 31) / 32 * 32;
+  for (int e = threadIdx.x; e < nq32 * (D / 32); e += kSelThreads) {
+    const int qi = e / (D / 32), part = e % (D / 32);
+    v4i code = {0, 0, 0, 0};
+    uint8_t sc = 0;
+    if (qi < nq) {
+      const int hq = hk * G + qi / a.R, r = qi % a.R;
+      const uint8_t* c = a.q.codes + b * a.q.cs[0] + hq * a.q.cs[1] + static_cast<int64_t>(r) * a.q.cs[2];
+      const uint8_t* s = a.q.scales + b * a.q.ss[0] + hq * a.q.ss[1] + static_cast<int64_t>(r) * a.q.ss[2];
+      code = *reinterpret_cast<const v4i*>(c + part * 16);
+      sc = s[part];
+    }
+    *reinterpret_cast<v4i*>(q_lds + qi * (D / 2) + part * 16) = code;
+    qs_lds[qi * (D / 32) + part] = sc;
+  }
+}
+
+// One 32-key block of K codes/scales for the MFMA (rows = keys, lane j:
+// key t0 + j, half hh), read through a buffer resource: keys past `t_hi`
+// read as zeros.
+template <int D>
+struct KBlock {
+  v4i op[D / 64];
+  int sc[D / 64];
+};
+
+template <int D>
+__device__ __forceinline__ KBlock<D> load_kblock(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int kcs,
+                                                 int kss, int t, int t_hi, int hh) {
+  KBlock<D> k;
+  const bool ok = t < t_hi;
+#pragma unroll
+  for (int dc = 0; dc < D / 64; ++dc) {
+    k.op[dc] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? static_cast<uint32_t>(t * kcs + dc * 32 + hh * 16)
+                                                            : 0x80000000u, 0, 0);
+    k.sc[dc] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? static_cast<uint32_t>(t * kss + 2 * dc + hh)
+                                                          : 0x80000000u, 0, 0);
+  }
+  return k;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sel_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Per (context chunk, batch x KV head): every recent query's partial row max
+// and row sum over the chunk.  The queries sit in LDS; wave w takes the
+// chunk's 32-key blocks w, w+4, ... for all query groups (K read once), and
+// the four waves' (max, sum) are merged in LDS at the end.
+constexpr int kStatGroups = kMaxRecent / 32;
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kMaxRecent * (D / 2)];
+  __shared__ uint8_t qs_lds[kMaxRecent * (D / 32)];
+  __shared__ float red[4][kMaxRecent][2];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 31, hh = lane >> 5;
-  const int qi = (qgrp * 4 + wave) * 32 + j;
   const int G = a.Hq / a.Hkv;
+  const int nq = G * a.R, ng = (nq + 31) / 32;
   const int ctx = clamp_ctx(a, b);
   const int t_lo = chunk * a.chunk;
   const int t_hi = min(t_lo + a.chunk, ctx);
-  if ((qgrp * 4 + wave) * 32 >= G * a.R) return;  // whole wave past the queries
-  v4i qop[D / 64];
-  int qsc[D / 64];
+  stage_queries<D>(a, b, hk, q_lds, qs_lds);
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rc = sel_rsrc(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], int64_t(ctx) * a.k.cs[2]);
+  const __amdgpu_buffer_rsrc_t rs = sel_rsrc(a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1], int64_t(ctx) * a.k.ss[2]);
+  const int kcs = static_cast<int>(a.k.cs[2]), kss = static_cast<int>(a.k.ss[2]);
+  float m[kStatGroups], l[kStatGroups];
 #pragma unroll
-  for (int dc = 0; dc < D / 64; ++dc) query_operand(a, b, hk, qi, hh, dc, qop[dc], qsc[dc]);
-  const uint8_t* kc = a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1];
-  const uint8_t* ks = a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1];
-  float m = -__builtin_huge_valf(), l = 0.0f;
-  for (int t0 = t_lo; t0 < t_hi; t0 += 32) {
-    const int t = t0 + j;
-    v16f s = v16f{};
-#pragma unroll
-    for (int dc = 0; dc < D / 64; ++dc) {
-      const bool ok = t < t_hi;
-      const v4i kop = ok ? *reinterpret_cast<const v4i*>(kc + static_cast<int64_t>(t) * a.k.cs[2] + dc * 32 + hh * 16)
-                         : v4i{0, 0, 0, 0};
-      const int ksc = ok ? ks[static_cast<int64_t>(t) * a.k.ss[2] + 2 * dc + hh] : 0;
-      s = mfma32_fp4(kop, qop[dc], s, ksc, qsc[dc]);
-    }
-    // Lane (query j, half hh) holds keys 8(r/4) + 4hh + r%4 of the block.
-    float x = -__builtin_huge_valf();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (key >= t_hi) s[r] = -__builtin_huge_valf();
-      x = fmaxf(x, s[r]);
-    }
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    const float m_new = fmaxf(m, x);
-    const float alpha = m == -__builtin_huge_valf() ? 0.0f : fast_exp2((m - m_new) * a.c);
-    const float mc = m_new * a.c;
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(s[r], a.c, -mc));
-    l = l * alpha + sum;
-    m = m_new;
+  for (int g = 0; g < kStatGroups; ++g) {
+    m[g] = -__builtin_huge_valf();
+    l[g] = 0.0f;
   }
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-  l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  if (hh == 0 && qi < G * a.R) {
+  int t0 = t_lo + wave * 32;
+  KBlock<D> kn = load_kblock<D>(rc, rs, kcs, kss, t0 + j, t_hi, hh);
+  for (; t0 < t_hi; t0 += 128) {
+    const KBlock<D> kb = kn;
+    kn = load_kblock<D>(rc, rs, kcs, kss, t0 + 128 + j, t_hi, hh);
+    // All query groups against this block; the key mask is compiled only
+    // into the form for a chunk's partial last block.
+    auto groups = [&](auto tail_tag) {
+      constexpr bool TAIL = decltype(tail_tag)::value;
+#pragma unroll
+      for (int g = 0; g < kStatGroups; ++g) {
+        if (g >= ng) continue;   // uniform; the loop stays unrolled, m[g]/l[g] in fixed registers
+        // B operand: query g*32 + j from LDS.
+        const int qi = g * 32 + j;
+        v16f s = v16f{};
+#pragma unroll
+        for (int dc = 0; dc < D / 64; ++dc) {
+          const v4i qop = *reinterpret_cast<const v4i*>(q_lds + qi * (D / 2) + dc * 32 + hh * 16);
+          const int qsc = qs_lds[qi * (D / 32) + 2 * dc + hh];
+          s = mfma32_fp4(kb.op[dc], qop, s, kb.sc[dc], qsc);
+        }
+        // Lane (query j, half hh) holds keys t0 + 8(r/4) + 4hh + r%4.
+        if constexpr (TAIL) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= t_hi) s[r] = -__builtin_huge_valf();
+        }
+        const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]), m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+        const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]), m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+        const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+        float x = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float m_new = fmaxf(m[g], x);
+        const float alpha = m[g] == -__builtin_huge_valf() ? 0.0f : fast_exp2((m[g] - m_new) * a.c);
+        const float mc = m_new * a.c;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(s[r], a.c, -mc));
+        l[g] = l[g] * alpha + sum;
+        m[g] = m_new;
+      }
+    };
+    if (t0 + 32 > t_hi) groups(std::true_type{});
+    else groups(std::false_type{});
+  }
+  // This wave's (max, sum) per query (the two lane halves hold halves of the
+  // sum), then the ordered merge of the four waves.
+#pragma unroll
+  for (int g = 0; g < kStatGroups; ++g) {
+    if (g >= ng) continue;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[g]), __float_as_uint(l[g]), false, false);
+    const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (hh == 0) {
+      red[wave][g * 32 + j][0] = m[g];
+      red[wave][g * 32 + j][1] = lt;
+    }
+  }
+  __syncthreads();
+  for (int qi = threadIdx.x; qi < nq; qi += kSelThreads) {
+    float M = -__builtin_huge_valf();
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][qi][0]);
+    float L = 0.0f;
+    for (int w = 0; w < 4; ++w)
+      if (red[w][qi][0] != -__builtin_huge_valf()) L += fast_exp2((red[w][qi][0] - M) * a.c) * red[w][qi][1];
     float* st = stat_slot(a, b, hk, qi, chunk);
-    st[0] = m;
-    st[1] = l;
+    st[0] = M;
+    st[1] = L;
   }
 }
 
@@ -134,87 +236,106 @@ __global__ __launch_bounds__(kSelThreads) void select_finalize_kernel(SelectArgs
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kCmKeys = 256;       // keys per colmass workgroup (4 waves x 2 blocks)
-constexpr int kMaxRecent = 512;    // recent queries x group size held in LDS
+// Per (512-key block, batch x KV head): the normalised probabilities of
+// every recent query of the group, summed per key and added to col_mass.
+// Lane (key j, half hh) of a 32x32 product holds 16 queries, in four runs of
+// four consecutive ones, so their (m c, 1/l) come from LDS as float4s.  Each
+// key belongs to one lane pair: no atomics.
+constexpr int kCmKeys = 512;
 
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kMaxRecent * (D / 2)];
   __shared__ uint8_t qs_lds[kMaxRecent * (D / 32)];
-  __shared__ float mst[kMaxRecent], inv_l[kMaxRecent];
+  __shared__ __attribute__((aligned(16))) float mc_lds[kMaxRecent + 32], il_lds[kMaxRecent + 32];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int nq = G * a.R;
+  const int nq = G * a.R, ng = (nq + 31) / 32;
   const int nchunk = (a.Tcap + a.chunk - 1) / a.chunk;
   const int ctx = clamp_ctx(a, b);
   const int k_lo = blk * kCmKeys;
   if (k_lo >= ctx) return;
-  // Stage the group's recent queries (codes, scales, max, 1/sum).
-  for (int e = threadIdx.x; e < nq * (D / 32); e += kSelThreads) {
-    const int qi = e / (D / 32), part = e % (D / 32);
-    const int hq = hk * G + qi / a.R, r = qi % a.R;
-    const uint8_t* c = a.q.codes + b * a.q.cs[0] + hq * a.q.cs[1] + static_cast<int64_t>(r) * a.q.cs[2];
-    const uint8_t* s = a.q.scales + b * a.q.ss[0] + hq * a.q.ss[1] + static_cast<int64_t>(r) * a.q.ss[2];
-    *reinterpret_cast<v4i*>(q_lds + qi * (D / 2) + part * 16) = *reinterpret_cast<const v4i*>(c + part * 16);
-    qs_lds[qi * (D / 32) + part] = s[part];
-  }
-  for (int qi = threadIdx.x; qi < nq; qi += kSelThreads) {
-    const float* st = stat_slot(a, b, hk, qi, nchunk);
-    mst[qi] = st[0];
-    inv_l[qi] = st[1];
+  const int k_hi = min(k_lo + kCmKeys, ctx);
+  stage_queries<D>(a, b, hk, q_lds, qs_lds);
+  for (int qi = threadIdx.x; qi < ng * 32; qi += kSelThreads) {
+    float mcv = 0.0f, il = 0.0f;   // padding queries contribute 0
+    if (qi < nq) {
+      const float* st = stat_slot(a, b, hk, qi, nchunk);
+      mcv = st[0] * a.c;
+      il = st[1];
+    }
+    mc_lds[qi] = mcv;
+    il_lds[qi] = il;
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 31, hh = lane >> 5;
-  const uint8_t* kc = a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1];
-  const uint8_t* ks = a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1];
+  const __amdgpu_buffer_rsrc_t rc = sel_rsrc(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], int64_t(ctx) * a.k.cs[2]);
+  const __amdgpu_buffer_rsrc_t rs = sel_rsrc(a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1], int64_t(ctx) * a.k.ss[2]);
+  const int kcs = static_cast<int>(a.k.cs[2]), kss = static_cast<int>(a.k.ss[2]);
   float* cm = a.col_mass + (static_cast<int64_t>(b) * a.Hkv + hk) * a.Tcap;
-  for (int kb = 0; kb < kCmKeys / 128; ++kb) {
-    const int t0 = k_lo + (kb * 4 + wave) * 32;
-    const int t = t0 + j;
-    if (t0 >= ctx) break;
-    const bool ok = t < ctx;
-    // B operand: key column j.
-    v4i kop[D / 64];
-    int ksc[D / 64];
-#pragma unroll
-    for (int dc = 0; dc < D / 64; ++dc) {
-      kop[dc] = ok ? *reinterpret_cast<const v4i*>(kc + static_cast<int64_t>(t) * a.k.cs[2] + dc * 32 + hh * 16)
-                   : v4i{0, 0, 0, 0};
-      ksc[dc] = ok ? ks[static_cast<int64_t>(t) * a.k.ss[2] + 2 * dc + hh] : 0;
-    }
+  int t0 = k_lo + wave * 32;
+  KBlock<D> kn = load_kblock<D>(rc, rs, kcs, kss, t0 + j, k_hi, hh);
+  for (; t0 < k_hi; t0 += 128) {
+    const KBlock<D> kb = kn;
+    kn = load_kblock<D>(rc, rs, kcs, kss, t0 + 128 + j, k_hi, hh);
     float colsum = 0.0f;
-    for (int q0 = 0; q0 < nq; q0 += 32) {
-      // A operand: queries q0 + (lane % 32).
-      const int qa = q0 + j;
+    for (int g = 0; g < ng; ++g) {
+      // A operand: queries g*32 + (lane % 32) from LDS.
+      const int qa = g * 32 + j;
       v16f s = v16f{};
 #pragma unroll
       for (int dc = 0; dc < D / 64; ++dc) {
-        v4i qop = {0, 0, 0, 0};
-        int qsc = 0;
-        if (qa < nq) {
-          qop = *reinterpret_cast<const v4i*>(q_lds + qa * (D / 2) + dc * 32 + hh * 16);
-          qsc = qs_lds[qa * (D / 32) + 2 * dc + hh];
-        }
-        s = mfma32_fp4(qop, kop[dc], s, qsc, ksc[dc]);
+        const v4i qop = *reinterpret_cast<const v4i*>(q_lds + qa * (D / 2) + dc * 32 + hh * 16);
+        const int qsc = qs_lds[qa * (D / 32) + 2 * dc + hh];
+        s = mfma32_fp4(qop, kb.op[dc], s, qsc, kb.sc[dc]);
       }
-      // Lane (key j, half hh) holds queries q0 + 8(r/4) + 4hh + r%4.
+      // Lane (key j, half hh) holds queries g*32 + 8(r/4) + 4hh + r%4.
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (qr < nq) colsum += fast_exp2(__builtin_fmaf(s[r], a.c, -mst[qr] * a.c)) * inv_l[qr];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int qb = g * 32 + 8 * q4 + 4 * hh;
+        const v4f mcv = *reinterpret_cast<const v4f*>(mc_lds + qb);
+        const v4f ilv = *reinterpret_cast<const v4f*>(il_lds + qb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          colsum = __builtin_fmaf(fast_exp2(__builtin_fmaf(s[4 * q4 + r], a.c, -mcv[r])), ilv[r], colsum);
       }
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(colsum), __float_as_uint(colsum), false, false);
     colsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (hh == 0 && ok) cm[t] += colsum;
+    const int t = t0 + j;
+    if (hh == 0 && t < k_hi) cm[t] += colsum;
   }
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectArgs a) {
-  __shared__ int hist[256];
-  __shared__ int scan_sel[kSelThreads], scan_eq[kSelThreads];
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+
+// Inclusive prefix sum over the 1024 threads of the workgroup (wave scans
+// with shuffles, then the 16 wave totals through LDS).
+__device__ __forceinline__ int block_scan_incl(int x, int* wtot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  __syncthreads();
+  return x + base;
+}
+
+// Per (batch, KV head): the k largest masses of the non-window prefix,
+// indices ascending, ties at the threshold to the lower indices.  One
+// workgroup of 1024 threads holds the masses in registers.
+template <int kTopkChunks>   // register capacity: kTopkChunks x 4096 keys
+__global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectArgs a) {
+  __shared__ int wtot[kTopkWaves];
   __shared__ uint32_t s_prefix;
   __shared__ int s_krem;
   const int bh = blockIdx.x;
@@ -225,92 +346,130 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectArgs a) 
   k = k > a.max_sel ? a.max_sel : k;
   const uint32_t* v = reinterpret_cast<const uint32_t*>(a.col_mass + static_cast<int64_t>(bh) * a.Tcap);
   int32_t* out = a.idx_out + static_cast<int64_t>(bh) * a.max_sel;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) {
     s_prefix = 0;
     s_krem = k;
     a.n_out[bh] = k;
   }
   __syncthreads();
-  uint32_t mask = 0;
+  // The masses stay in registers for all passes: entry c*4096 + 4*tid + u
+  // in x[c][u].
+  uint32_t x[kTopkChunks][4];
+  const int nch = (n + kTopkThreads * 4 - 1) / (kTopkThreads * 4);
+#pragma unroll
+  for (int c = 0; c < kTopkChunks; ++c)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c * kTopkThreads * 4 + tid * 4 + u;
+      x[c][u] = (c < nch && i < n) ? v[i] : 0u;
+    }
+  // Threshold: the largest bit pattern tau with at least k entries >= tau,
+  // found bit by bit from the top (fp32 bit patterns of non-negative values
+  // order like the values); each step is one count over the registers.
+  auto count_ge = [&](uint32_t cand) -> int {
+    int c = 0;
+#pragma unroll
+    for (int cc = 0; cc < kTopkChunks; ++cc) {
+      if (cc >= nch) break;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = cc * kTopkThreads * 4 + tid * 4 + u;
+        c += (i < n && x[cc][u] >= cand) ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) wtot[wave] = c;
+    __syncthreads();
+    int total = 0;
+    for (int w = 0; w < kTopkWaves; ++w) total += wtot[w];
+    __syncthreads();
+    return total;
+  };
+  uint32_t tau_bits = 0;
   if (k > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      const uint32_t prefix = s_prefix;
-      for (int i = tid; i < n; i += kSelThreads) {
-        const uint32_t x = v[i];
-        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 0xFF], 1);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int krem = s_krem, above = 0, bin = 255;
-        for (; bin > 0; --bin) {
-          if (above + hist[bin] >= krem) break;
-          above += hist[bin];
-        }
-        s_krem = krem - above;
-        s_prefix = prefix | (static_cast<uint32_t>(bin) << shift);
-      }
-      mask |= 0xFFu << shift;
-      __syncthreads();
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = tau_bits | (1u << bit);
+      if (count_ge(cand) >= k) tau_bits = cand;
+    }
+    const int above = tau_bits == 0x7FFFFFFFu ? 0 : count_ge(tau_bits + 1);
+    if (tid == 0) {
+      s_prefix = tau_bits;
+      s_krem = k - above;
     }
   }
+  __syncthreads();
   const uint32_t tau = s_prefix;
-  const int take_eq = s_krem;  // equal-to-threshold entries to keep, lowest indices first
+  const int take_eq = s_krem;  // entries equal to the threshold to keep, lowest indices first
+  // Ordered compaction, chunk by chunk; ranks within a wave from ballots,
+  // across waves from the wave totals.
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int base_sel = 0, base_eq = 0;
-  for (int c0 = 0; c0 < n && k > 0; c0 += kSelThreads * 4) {
-    int fsel[4], feq[4], lsel = 0, leq = 0;
+#pragma unroll
+  for (int c = 0; c < kTopkChunks; ++c) {
+    if (c >= nch || k == 0) break;
+    const int c0 = c * kTopkThreads * 4;
+    bool gt[4], eq[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = c0 + tid * 4 + u;
-      const uint32_t x = i < n ? v[i] : 0u;
-      feq[u] = (i < n && x == tau) ? 1 : 0;
-      fsel[u] = (i < n && x > tau) ? 1 : 0;
-      leq += feq[u];
+      gt[u] = i < n && x[c][u] > tau;
+      eq[u] = i < n && x[c][u] == tau;
     }
-    scan_eq[tid] = leq;
-    __syncthreads();
-    for (int off = 1; off < kSelThreads; off <<= 1) {  // inclusive scan of equal counts
-      const int add = tid >= off ? scan_eq[tid - off] : 0;
-      __syncthreads();
-      scan_eq[tid] += add;
-      __syncthreads();
-    }
-    int eq_rank = base_eq + scan_eq[tid] - leq;
+    // Rank of each equal entry among the equal entries (index order).
+    int eq_before = 0, eq_mine = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (feq[u]) {
-        fsel[u] = eq_rank < take_eq ? 1 : 0;
-        ++eq_rank;
-      }
-      lsel += fsel[u];
+      eq_before += __popcll(__ballot(eq[u]) & lt);
+      eq_mine += eq[u] ? 1 : 0;
     }
-    scan_sel[tid] = lsel;
+    if (lane == 63) wtot[wave] = eq_before + eq_mine;
     __syncthreads();
-    for (int off = 1; off < kSelThreads; off <<= 1) {
-      const int add = tid >= off ? scan_sel[tid - off] : 0;
-      __syncthreads();
-      scan_sel[tid] += add;
-      __syncthreads();
+    int eq_base = base_eq, eq_total = 0;
+    for (int w = 0; w < kTopkWaves; ++w) {
+      if (w < wave) eq_base += wtot[w];
+      eq_total += wtot[w];
     }
-    int pos = base_sel + scan_sel[tid] - lsel;
+    __syncthreads();
+    bool sel[4];
+    int r_eq = eq_base + eq_before;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sel[u] = gt[u];
+      if (eq[u]) {
+        sel[u] = r_eq < take_eq;
+        ++r_eq;
+      }
+    }
+    int sel_before = 0, sel_mine = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sel_before += __popcll(__ballot(sel[u]) & lt);
+      sel_mine += sel[u] ? 1 : 0;
+    }
+    if (lane == 63) wtot[wave] = sel_before + sel_mine;
+    __syncthreads();
+    int pos = base_sel + sel_before, sel_total = 0;
+    for (int w = 0; w < kTopkWaves; ++w) {
+      if (w < wave) pos += wtot[w];
+      sel_total += wtot[w];
+    }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (fsel[u]) out[pos++] = c0 + tid * 4 + u;
-    base_sel += scan_sel[kSelThreads - 1];
-    base_eq += scan_eq[kSelThreads - 1];
-    __syncthreads();
+      if (sel[u]) out[pos++] = c0 + tid * 4 + u;
+    base_sel += sel_total;
+    base_eq += eq_total;
   }
-  for (int i = k + tid; i < a.max_sel; i += kSelThreads) out[i] = -1;
+  for (int i = k + tid; i < a.max_sel; i += kTopkThreads) out[i] = -1;
 }
 
 hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   if (a.R > 0) {
     const int nchunk = (a.Tcap + a.chunk - 1) / a.chunk;
-    const int qgroups = (G * a.R + 127) / 128;
-    const dim3 g1(nchunk, qgroups, a.B * a.Hkv);
+    const dim3 g1(nchunk, a.B * a.Hkv);
     const int nq = a.B * a.Hkv * G * a.R;
     const dim3 g3((a.Tcap + kCmKeys - 1) / kCmKeys, a.B * a.Hkv);
     if (D == 128) {
@@ -325,7 +484,12 @@ hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream) {
       hipLaunchKernelGGL(select_colmass_kernel<64>, g3, dim3(kSelThreads), 0, stream, a);
     }
   }
-  hipLaunchKernelGGL(select_topk_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), 0, stream, a);
+  // Contexts up to 32K keep 32 masses per thread in registers; longer ones
+  // (up to 64K) hold 64, part of them spilled.
+  if (a.Tcap <= 8 * kTopkThreads * 4)
+    hipLaunchKernelGGL(select_topk_kernel<8>, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(select_topk_kernel<16>, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 

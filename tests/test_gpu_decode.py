@@ -199,13 +199,15 @@ def test_hybrid_decode_workload_4_full_size():
 
 
 # ------------------------------------------------------------------ selection
-def test_topk_exact_on_given_masses():
+@pytest.mark.parametrize("tcap", [5000, 40000])
+def test_topk_exact_on_given_masses(tcap):
     """R = 0: only the top-k runs, on integer-valued masses with many ties;
-    the indices must equal the oracle's exactly."""
+    the indices must equal the oracle's exactly.  Contexts above 32K take the
+    second register layout of the selection."""
     rng = np.random.default_rng(41)
-    b, hkv, tcap = 3, 2, 5000
+    b, hkv = 3, 2
     cm = rng.integers(0, 50, size=(b, hkv, tcap)).astype(np.float32)
-    ctx = np.array([5000, 3001, 129], dtype=np.int32)
+    ctx = np.array([tcap, (3 * tcap) // 5 + 1, 129], dtype=np.int32)
     kc = mxa.empty_mx((b, hkv, tcap, 128), "hd", DEV)
     col = torch.from_numpy(cm).to(DEV)
     idx, n = mxa.select_vertical(None, kc, torch.from_numpy(ctx).to(DEV), col, window=128,
