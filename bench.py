@@ -36,8 +36,8 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # fetch 7220 KiB x 2.000 + write 65607 KiB x 1.000 per dispatch
-    "prefill_kernel<128,128,true>": {"bytes": 81968323, "sources": "68aeba6ca671a0f1"},
+    # fetch 7032 KiB x 2.000 + write 65762 KiB x 1.000 per dispatch
+    "prefill_kernel<128,128,true,true>": {"bytes": 81741318, "sources": "0b7d5efac66e89d4"},
     # fetch 557414 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch
     "decode_scan_kernel<128> split 4096": {"bytes": 1146007569, "sources": "585a6817441207fd"},
 }
@@ -351,11 +351,11 @@ def main():
                                "bf16 N(0,1) with 4 K channels x12 per KV head, static Smooth-QK, OCP scales, "
                                f"P-Reordering/PNQ, kv_tile {args.kv_tile}; step = quantise Q,K,V + attention",
                    "global_batch": 1, "seq_len": 4096, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,128,causal>",
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,128,causal,pnq>",
                      "achieved": round(pre["kernel_tflops"], 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre["kernel_tflops"] / PEAK_FP4_TFLOPS, 4),
                      "kernel_ms": round(pre["kernel_s"] * 1e3, 4),
-                     "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,true>")},
+                     "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,true,true>")},
     }
     del d
     torch.cuda.empty_cache()
