@@ -124,10 +124,12 @@ def prefill_leg(args):
     def attn():
         mxa.prefill(qh, kh, vh, causal=True, kv_tile=args.kv_tile, out=out)
 
+    # Q, K (with their Smooth-QK factors) and V quantised by one launch.
+    qkv_jobs = [dict(x=d["q"], chan_scale=qs, out=qh), dict(x=d["k"], chan_scale=ks, out=kh),
+                dict(x=d["v"], layout="key", out=vh)]
+
     def step():
-        mxa.quantize(d["q"], "hd", chan_scale=qs, out=qh)
-        mxa.quantize(d["k"], "hd", chan_scale=ks, out=kh)
-        mxa.quantize(d["v"], "key", out=vh)
+        mxa.quantize_batch(qkv_jobs)
         attn()
 
     wall, kern = timed(step, args.steps, args.warmup, attn)

@@ -47,6 +47,17 @@ class _Mx(ctypes.Structure):
     ]
 
 
+class _QuantJob(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("x_stride", ctypes.c_int64 * 3), ("chan_scale", ctypes.c_void_p),
+        ("rule", ctypes.c_int32), ("qmax", ctypes.c_float), ("out", ctypes.POINTER(_Mx)),
+    ]
+
+
+MAX_QUANTIZE_JOBS = 4
+
+
 class _PrefillParams(ctypes.Structure):
     _fields_ = [
         ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
@@ -72,6 +83,7 @@ def _load():
     P = ctypes.POINTER
     sig = {
         "mxattn_quantize": [vp, i32, P(i64), vp, i32, f32, P(_Mx), vp],
+        "mxattn_quantize_batch": [P(_QuantJob), i32, vp],
         "mxattn_smooth_calibrate": [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp],
         "mxattn_prefill": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), vp, i32, vp, vp],
         "mxattn_decode": [P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
@@ -97,7 +109,7 @@ _lib = _load()
 
 # Every symbol the C header declares (checked by the CPU tests).
 EXPORTS = (
-    "mxattn_quantize", "mxattn_smooth_calibrate", "mxattn_prefill",
+    "mxattn_quantize", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
     "mxattn_decode_workspace_bytes", "mxattn_decode",
     "mxattn_select_workspace_bytes", "mxattn_select_vertical",
     "mxattn_status_string", "mxattn_last_error", "mxattn_version",
@@ -184,6 +196,37 @@ def quantize(x, layout="hd", chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=Non
     _check(_lib.mxattn_quantize(_ptr(x), _DT[x.dtype], strides, _ptr(cs), _RULES[rule],
                                 float(qmax), ctypes.byref(d), _stream(x)))
     return out
+
+
+def quantize_batch(jobs):
+    """Several quantize() calls in one launch.  jobs: list of dicts with the
+    keyword arguments of quantize() (x required; layout, chan_scale, rule,
+    qmax, out optional).  Returns the outputs in job order; bit-identical to
+    one quantize() per job."""
+    assert 1 <= len(jobs) <= MAX_QUANTIZE_JOBS, f"1..{MAX_QUANTIZE_JOBS} jobs"
+    arr = (_QuantJob * len(jobs))()
+    keep, outs = [], []
+    for i, j in enumerate(jobs):
+        x = j["x"]
+        assert x.dim() == 4 and x.stride(3) == 1, "x must be [B,H,S,D] with contiguous D"
+        out = j.get("out")
+        if out is None:
+            out = empty_mx(tuple(x.shape), j.get("layout", "hd"), x.device)
+        cs = j.get("chan_scale")
+        if cs is not None:
+            cs = cs.to(torch.float32).contiguous()
+        d = out.desc()
+        keep += [cs, d]
+        arr[i].x = _ptr(x)
+        arr[i].x_dtype = _DT[x.dtype]
+        arr[i].x_stride[:] = [x.stride(0), x.stride(1), x.stride(2)]
+        arr[i].chan_scale = _ptr(cs)
+        arr[i].rule = _RULES[j.get("rule", "ocp")]
+        arr[i].qmax = float(j.get("qmax", UOS_QMAX))
+        arr[i].out = ctypes.pointer(d)
+        outs.append(out)
+    _check(_lib.mxattn_quantize_batch(arr, len(jobs), _stream(jobs[0]["x"])))
+    return outs
 
 
 def smooth_calibrate(q_cal, k_cal):

@@ -20,6 +20,8 @@
 #include "../../include/mxattn.h"
 #include "kernels.h"
 
+static_assert(MXATTN_MAX_QUANTIZE_JOBS == mxattn::kMaxQuantJobs, "batch size limits differ");
+
 using namespace mxattn;
 
 namespace {
@@ -78,6 +80,10 @@ mxattn_status_t check_mx(const mxattn_mx_t* t, const char* name, int want_layout
     return fail(MXATTN_ERR_INVALID_ARG, "%s: empty shape [%lld,%lld,%lld,%lld]", name, (long long)t->batch,
                 (long long)t->heads, (long long)t->seq, (long long)t->dim);
   if (t->dim != 64 && t->dim != 128) return fail(MXATTN_ERR_UNSUPPORTED, "%s: head_dim %lld not in {64,128}", name, (long long)t->dim);
+  // Batch and heads index grid dimensions y and z; positions inside one head
+  // are 32-bit in the kernels.
+  if (t->batch > 65535 || t->heads > 65535 || t->seq > (int64_t{1} << 26))
+    return fail(MXATTN_ERR_UNSUPPORTED, "%s: batch/heads above 65535 or seq above 2^26", name);
   if (!aligned16(t->codes)) return fail(MXATTN_ERR_INVALID_ARG, "%s: codes not 16-byte aligned", name);
   for (int i = 0; i < 3; ++i)
     if (t->code_stride[i] < 0 || t->code_stride[i] % 16 != 0 || t->scale_stride[i] < 0)
@@ -126,46 +132,75 @@ const char* mxattn_status_string(mxattn_status_t s) {
   return "unknown status";
 }
 
+// Validates one quantisation request and fills its kernel arguments.
+static mxattn_status_t quantize_args(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
+                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                     const mxattn_mx_t* out, const char* name, QuantArgs* a) {
+  mxattn_status_t st;
+  if (x == nullptr || x_stride == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "%s: null input", name);
+  if (x_dtype != MXATTN_F32 && x_dtype != MXATTN_F16 && x_dtype != MXATTN_BF16)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)x_dtype);
+  if (rule != MXATTN_SCALE_OCP && rule != MXATTN_SCALE_UOS) return fail(MXATTN_ERR_INVALID_ARG, "%s: unknown rule", name);
+  if (rule == MXATTN_SCALE_UOS && !valid_qmax(qmax))
+    return fail(MXATTN_ERR_UNSUPPORTED, "%s: UOS qmax must lie in (4, 8)", name);
+  if ((st = check_mx(out, name, -1)) != MXATTN_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if (x_stride[i] < 0) return fail(MXATTN_ERR_INVALID_ARG, "%s: negative input stride", name);
+  // Rows are read 8 elements (16 or 32 bytes) at a time.
+  const int esz = x_dtype == MXATTN_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(x) % 16) != 0 || (x_stride[0] * esz) % 16 != 0 || (x_stride[1] * esz) % 16 != 0 ||
+      (x_stride[2] * esz) % 16 != 0)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: input and its row strides must be 16-byte aligned", name);
+  if (chan_scale != nullptr && (reinterpret_cast<uintptr_t>(chan_scale) % 16) != 0)
+    return fail(MXATTN_ERR_INVALID_ARG, "%s: chan_scale must be 16-byte aligned", name);
+  *a = QuantArgs{};
+  a->x = x;
+  a->dtype = x_dtype == MXATTN_F32 ? 0 : (x_dtype == MXATTN_F16 ? 1 : 2);
+  for (int i = 0; i < 3; ++i) {
+    a->xs[i] = x_stride[i];
+    a->cs[i] = out->code_stride[i];
+    a->ss[i] = out->scale_stride[i];
+  }
+  a->chan_scale = chan_scale;
+  a->uos = rule == MXATTN_SCALE_UOS;
+  a->qmax_quarter = qmax * 0.25f;
+  a->key_layout = out->layout == MXATTN_LAYOUT_KEY;
+  a->B = out->batch;
+  a->H = out->heads;
+  a->S = out->seq;
+  a->D = out->dim;
+  a->codes = out->codes;
+  a->scales = out->scales;
+  return MXATTN_OK;
+}
+
 mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
                                 const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
                                 const mxattn_mx_t* out, mxattn_stream_t stream) {
   mxattn_status_t st;
   if (injected("quantize", &st)) return st;
-  if (x == nullptr || x_stride == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "quantize: null input");
-  if (x_dtype != MXATTN_F32 && x_dtype != MXATTN_F16 && x_dtype != MXATTN_BF16)
-    return fail(MXATTN_ERR_INVALID_ARG, "quantize: unknown dtype %d", (int)x_dtype);
-  if (rule != MXATTN_SCALE_OCP && rule != MXATTN_SCALE_UOS) return fail(MXATTN_ERR_INVALID_ARG, "quantize: unknown rule");
-  if (rule == MXATTN_SCALE_UOS && !valid_qmax(qmax)) return fail(MXATTN_ERR_UNSUPPORTED, "quantize: UOS qmax must lie in (4, 8)");
-  if ((st = check_mx(out, "quantize.out", -1)) != MXATTN_OK) return st;
-  for (int i = 0; i < 3; ++i)
-    if (x_stride[i] < 0) return fail(MXATTN_ERR_INVALID_ARG, "quantize: negative input stride");
-  // Rows are read 8 elements (16 or 32 bytes) at a time.
-  const int esz = x_dtype == MXATTN_F32 ? 4 : 2;
-  if ((reinterpret_cast<uintptr_t>(x) % 16) != 0 || (x_stride[0] * esz) % 16 != 0 || (x_stride[1] * esz) % 16 != 0 ||
-      (x_stride[2] * esz) % 16 != 0)
-    return fail(MXATTN_ERR_INVALID_ARG, "quantize: input and its row strides must be 16-byte aligned");
-  if (chan_scale != nullptr && (reinterpret_cast<uintptr_t>(chan_scale) % 16) != 0)
-    return fail(MXATTN_ERR_INVALID_ARG, "quantize: chan_scale must be 16-byte aligned");
-  QuantArgs a{};
-  a.x = x;
-  a.dtype = x_dtype == MXATTN_F32 ? 0 : (x_dtype == MXATTN_F16 ? 1 : 2);
-  for (int i = 0; i < 3; ++i) {
-    a.xs[i] = x_stride[i];
-    a.cs[i] = out->code_stride[i];
-    a.ss[i] = out->scale_stride[i];
-  }
-  a.chan_scale = chan_scale;
-  a.uos = rule == MXATTN_SCALE_UOS;
-  a.qmax_quarter = qmax * 0.25f;
-  a.key_layout = out->layout == MXATTN_LAYOUT_KEY;
-  a.B = out->batch;
-  a.H = out->heads;
-  a.S = out->seq;
-  a.D = out->dim;
-  a.codes = out->codes;
-  a.scales = out->scales;
+  QuantArgs a;
+  if ((st = quantize_args(x, x_dtype, x_stride, chan_scale, rule, qmax, out, "quantize", &a)) != MXATTN_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(launch_quantize(a, s), s, "quantize");
+  return after_launch(launch_quantize_batch(&a, 1, s), s, "quantize");
+}
+
+mxattn_status_t mxattn_quantize_batch(const mxattn_quantize_job_t* jobs, int32_t n_jobs, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("quantize_batch", &st)) return st;
+  if (jobs == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "quantize_batch: null job list");
+  if (n_jobs < 1 || n_jobs > MXATTN_MAX_QUANTIZE_JOBS)
+    return fail(MXATTN_ERR_INVALID_ARG, "quantize_batch: n_jobs %d not in [1, %d]", (int)n_jobs, MXATTN_MAX_QUANTIZE_JOBS);
+  QuantArgs a[MXATTN_MAX_QUANTIZE_JOBS];
+  for (int i = 0; i < n_jobs; ++i) {
+    char name[40];
+    snprintf(name, sizeof(name), "quantize_batch.job[%d]", i);
+    const mxattn_quantize_job_t& j = jobs[i];
+    if ((st = quantize_args(j.x, j.x_dtype, j.x_stride, j.chan_scale, j.rule, j.qmax, j.out, name, &a[i])) != MXATTN_OK)
+      return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_quantize_batch(a, n_jobs, s), s, "quantize_batch");
 }
 
 mxattn_status_t mxattn_smooth_calibrate(const void* q_cal, const void* k_cal, mxattn_dtype_t dtype, int64_t hq,

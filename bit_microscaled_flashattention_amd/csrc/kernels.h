@@ -22,6 +22,17 @@ struct QuantArgs {
   int64_t ss[3];
 };
 
+// Up to kMaxQuantJobs tensors quantised by one launch; start[i] is the first
+// workgroup of job i and start[n] the grid size, gx[i] the workgroups along
+// the sequence of one (batch, head) of job i.
+constexpr int kMaxQuantJobs = 4;
+struct QuantBatch {
+  QuantArgs job[kMaxQuantJobs];
+  int start[kMaxQuantJobs + 1];
+  int gx[kMaxQuantJobs];
+  int n;
+};
+
 struct CalibArgs {
   const void* q;
   const void* k;
@@ -93,7 +104,7 @@ struct SelectArgs {
   int32_t* n_out;
 };
 
-hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_quantize_batch(const QuantArgs* jobs, int n, hipStream_t stream);
 hipError_t launch_smooth_calibrate(const CalibArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream);

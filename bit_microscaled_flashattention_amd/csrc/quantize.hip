@@ -43,9 +43,6 @@ __device__ __forceinline__ void load8(const void* base, int64_t i, float* y) {
 }
 
 // ---------------------------------------------------------------------------
-// Head-dim blocks.  Four lanes own one 32-element block (8 elements each, one
-// 16-byte load for 16-bit inputs), so a wave covers 16 consecutive blocks and
-// every load and store is contiguous across the wave.
 // Eight elements to eight packed E2M1 codes (element i in nibble i) under
 // scale byte sb.  From byte 3 up the hardware convert does it: it rounds
 // y/2^e to nearest even on the E2M1 grid, saturates and keeps the sign, and
@@ -67,118 +64,174 @@ __device__ __forceinline__ uint32_t encode8(const float* y, int sb) {
   return packed;
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void quantize_hd_kernel(QuantArgs a) {
-  const int64_t nblk_row = a.D / 32;
-  const int64_t total = a.B * a.H * a.S * nblk_row;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t blk = gid >> 2;
-  const int part = static_cast<int>(gid & 3);
-  // Lanes past the end still take part in the cross-lane maximum (with a
-  // zero contribution) and then write nothing.
-  const bool live = blk < total;
-  const int64_t bb = live ? blk : 0;
-  const int64_t db = bb % nblk_row;
-  int64_t rest = bb / nblk_row;
-  const int64_t s = rest % a.S;
-  rest /= a.S;
-  const int64_t h = rest % a.H;
-  const int64_t b = rest / a.H;
-  const int64_t d0 = db * 32 + part * 8;
+// ---------------------------------------------------------------------------
+// Head-dim blocks.  Four lanes own one 32-element block (8 elements each, one
+// 16-byte load for 16-bit inputs), so one load instruction of a wave covers
+// 16 consecutive blocks contiguously.  Each lane handles kHdRows such
+// groups, all loads issued before any arithmetic; the block maximum is
+// combined over the four lanes with two quad permutes.  Workgroup x of
+// (batch b, head h) covers blocks [x*64*kHdRows, (x+1)*64*kHdRows) of that
+// head; the index arithmetic inside a head is 32-bit.
+constexpr int kHdRows = 2;
+constexpr int kHdBlocksPerGroup = 64 * kHdRows;   // 4 waves x 16 blocks x kHdRows
 
-  float y[8];
-  if (live) {
-    load8<DT>(a.x, b * a.xs[0] + h * a.xs[1] + s * a.xs[2] + d0, y);
-    if (a.chan_scale != nullptr) {
-      const v4f c0 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0);
-      const v4f c1 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0 + 4);
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]: after both, every lane of a quad
+  // holds the maximum of the four.
+  uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+  v = o > v ? o : v;
+  o = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+  return o > v ? o : v;
+}
+
+template <int DT>
+__device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h, int64_t b) {
+  const int nblk_row = static_cast<int>(a.D) / 32;   // 2 or 4
+  const int total = static_cast<int>(a.S) * nblk_row;
+  const int lane = threadIdx.x & 63;
+  const int wave = x * 4 + (threadIdx.x >> 6);
+  const int part = lane & 3;
+  const int64_t head_off = b * a.xs[0] + h * a.xs[1];
+
+  float y[kHdRows][8];
+#pragma unroll
+  for (int r = 0; r < kHdRows; ++r) {
+    const int blk = (wave * kHdRows + r) * 16 + (lane >> 2);
+    if (blk < total) {
+      const int64_t s = blk / nblk_row;
+      load8<DT>(a.x, head_off + s * a.xs[2] + ((blk & (nblk_row - 1)) * 32 + part * 8), y[r]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[r][k] = 0.0f;
+    }
+  }
+  // Groups of 16 blocks start on a row boundary (nblk_row divides 16), so a
+  // lane's channels are the same in every group it handles.
+  const int db = (lane >> 2) & (nblk_row - 1);
+  const int d0 = db * 32 + part * 8;
+  if (a.chan_scale != nullptr) {
+    const v4f c0 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0);
+    const v4f c1 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0 + 4);
+#pragma unroll
+    for (int r = 0; r < kHdRows; ++r)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        y[k] = __fmul_rn(y[k], c0[k]);
-        y[4 + k] = __fmul_rn(y[4 + k], c1[k]);
+        y[r][k] = __fmul_rn(y[r][k], c0[k]);
+        y[r][4 + k] = __fmul_rn(y[r][4 + k], c1[k]);
       }
+  }
+#pragma unroll
+  for (int r = 0; r < kHdRows; ++r) {
+    const int blk = (wave * kHdRows + r) * 16 + (lane >> 2);
+    const int64_t s = blk / nblk_row;
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = __float_as_uint(y[r][i]) & 0x7FFFFFFFu;
+      amax = m > amax ? m : amax;  // magnitudes order like their bit patterns
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = 0.0f;
+    // Lanes of a quad share blk, so a quad past the end is dead as a whole.
+    amax = quad_max(amax);
+    const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
+    const uint32_t packed = encode8(y[r], sb);
+    if (blk >= total) continue;
+    uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + s * a.cs[2];
+    *reinterpret_cast<uint32_t*>(crow + d0 / 2) = packed;
+    if (part == 0) a.scales[b * a.ss[0] + h * a.ss[1] + s * a.ss[2] + db] = static_cast<uint8_t>(sb);
   }
-  uint32_t amax = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t m = __float_as_uint(y[i]) & 0x7FFFFFFFu;
-    amax = m > amax ? m : amax;  // magnitudes order like their bit patterns
-  }
-  uint32_t o1 = __shfl_xor(amax, 1, 4);
-  amax = o1 > amax ? o1 : amax;
-  uint32_t o2 = __shfl_xor(amax, 2, 4);
-  amax = o2 > amax ? o2 : amax;
-  const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
-  const uint32_t packed = encode8(y, sb);
-  if (!live) return;
-  uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + s * a.cs[2];
-  *reinterpret_cast<uint32_t*>(crow + d0 / 2) = packed;
-  if (part == 0) a.scales[b * a.ss[0] + h * a.ss[1] + s * a.ss[2] + db] = static_cast<uint8_t>(sb);
 }
 
 // ---------------------------------------------------------------------------
-// Sequence blocks (the key-blocked V layout of prefill).  A workgroup stages
-// 64 tokens x D channels in LDS as fp32 (16-byte loads along the channels),
-// then each thread encodes one (channel, 32-token block) and writes its 16
-// code bytes.  Tokens past S are +0 padding inside the last block.
-constexpr int kKeyChunk = 64;
+// Sequence blocks (the key-blocked V layout of prefill).  Workgroup x of
+// (b, h) stages tokens [32x, 32x+32) x D channels in LDS as fp32 (16-byte
+// loads along the channels, all issued before the first LDS store), then
+// each of the first D threads encodes one (channel, 32-token block) and
+// writes its 16 code bytes.  Tokens past S are +0 padding inside the last
+// block.
+constexpr int kKeyChunk = 32;
+constexpr int kKeyLoads = kKeyChunk * 16 / 256;  // 8-element loads per thread at D = 128
 
 template <int DT>
-__global__ __launch_bounds__(256) void quantize_key_kernel(QuantArgs a) {
-  __shared__ float tile[kKeyChunk][129];
-  const int64_t nchunk = (a.S + kKeyChunk - 1) / kKeyChunk;
-  const int64_t chunk = blockIdx.x % nchunk;
-  const int64_t bh = blockIdx.x / nchunk;
-  const int64_t h = bh % a.H;
-  const int64_t b = bh / a.H;
+__device__ __forceinline__ void quantize_key(const QuantArgs& a, int x, int64_t h, int64_t b,
+                                             float (*tile)[129]) {
   const int D = static_cast<int>(a.D);
-  const int64_t t0 = chunk * kKeyChunk;
+  const int64_t t0 = static_cast<int64_t>(x) * kKeyChunk;
   const int groups = D / 8;  // 8-channel groups per token
-  for (int i = threadIdx.x; i < kKeyChunk * groups; i += blockDim.x) {
+  float y[kKeyLoads][8];
+#pragma unroll
+  for (int j = 0; j < kKeyLoads; ++j) {
+    const int i = threadIdx.x + j * 256;
     const int tt = i / groups, d0 = (i % groups) * 8;
     const int64_t t = t0 + tt;
-    float y[8];
-    if (t < a.S) {
-      load8<DT>(a.x, b * a.xs[0] + h * a.xs[1] + t * a.xs[2] + d0, y);
-      if (a.chan_scale != nullptr) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(y[k], a.chan_scale[h * a.D + d0 + k]);
-      }
+    if (i < kKeyChunk * groups && t < a.S) {
+      load8<DT>(a.x, b * a.xs[0] + h * a.xs[1] + t * a.xs[2] + d0, y[j]);
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = 0.0f;
+      for (int k = 0; k < 8; ++k) y[j][k] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kKeyLoads; ++j) {
+    const int i = threadIdx.x + j * 256;
+    if (i >= kKeyChunk * groups) continue;
+    const int tt = i / groups, d0 = (i % groups) * 8;
+    if (a.chan_scale != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[j][k] = __fmul_rn(y[j][k], a.chan_scale[h * a.D + d0 + k]);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) tile[tt][d0 + k] = y[k];
+    for (int k = 0; k < 8; ++k) tile[tt][d0 + k] = y[j][k];
   }
   __syncthreads();
-  const int tasks = D * (kKeyChunk / 32);
-  for (int task = threadIdx.x; task < tasks; task += blockDim.x) {
-    const int d = task % D;
-    const int sub = task / D;
-    const int64_t tblk = t0 / 32 + sub;
-    if (tblk * 32 >= a.S) continue;
-    uint32_t amax = 0;
-    for (int i = 0; i < 32; ++i) {
-      uint32_t m = __float_as_uint(tile[sub * 32 + i][d]) & 0x7FFFFFFFu;
-      amax = m > amax ? m : amax;
-    }
-    const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
-    uint32_t w[4];
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  uint32_t amax = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float y[8];
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t m = __float_as_uint(tile[i][d]) & 0x7FFFFFFFu;
+    amax = m > amax ? m : amax;
+  }
+  const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
+  uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = tile[sub * 32 + q * 8 + i][d];
-      w[q] = encode8(y, sb);
-    }
-    uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + static_cast<int64_t>(d) * a.cs[2];
-    *reinterpret_cast<v4i*>(crow + tblk * 16) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    a.scales[b * a.ss[0] + h * a.ss[1] + static_cast<int64_t>(d) * a.ss[2] + tblk] = static_cast<uint8_t>(sb);
+  for (int q = 0; q < 4; ++q) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = tile[q * 8 + i][d];
+    w[q] = encode8(v, sb);
+  }
+  uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + static_cast<int64_t>(d) * a.cs[2];
+  *reinterpret_cast<v4i*>(crow + x * 16) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  a.scales[b * a.ss[0] + h * a.ss[1] + static_cast<int64_t>(d) * a.ss[2] + x] = static_cast<uint8_t>(sb);
+}
+
+// ---------------------------------------------------------------------------
+// One launch for up to kMaxQuantJobs tensors.  The grid is the concatenation
+// of the jobs' workgroup ranges; workgroup id -> (job, x, head, batch) is
+// uniform scalar arithmetic.  A single small tensor does not fill the chip
+// and pays a launch's ramp and drain on its own: batched, the tensors of one
+// attention call share them.
+__global__ __launch_bounds__(256) void quantize_kernel(QuantBatch p) {
+  __shared__ float tile[kKeyChunk][129];
+  const int bid = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxQuantJobs; ++i) j += (i < p.n && bid >= p.start[i]) ? 1 : 0;
+  const QuantArgs& a = p.job[j];
+  const int local = bid - p.start[j];
+  const int gx = p.gx[j];
+  const int x = local % gx;
+  const int rest = local / gx;
+  const int H = static_cast<int>(a.H);
+  const int64_t h = rest % H, b = rest / H;
+  if (a.key_layout) {
+    if (a.dtype == 2) quantize_key<2>(a, x, h, b, tile);
+    else if (a.dtype == 1) quantize_key<1>(a, x, h, b, tile);
+    else quantize_key<0>(a, x, h, b, tile);
+  } else {
+    if (a.dtype == 2) quantize_hd<2>(a, x, h, b);
+    else if (a.dtype == 1) quantize_hd<1>(a, x, h, b);
+    else quantize_hd<0>(a, x, h, b);
   }
 }
 
@@ -220,23 +273,30 @@ __global__ __launch_bounds__(256) void smooth_calibrate_kernel(CalibArgs a) {
   }
 }
 
-template <int DT>
-static void launch_quantize_t(const QuantArgs& a, hipStream_t stream) {
-  if (a.key_layout) {
-    const int64_t nchunk = (a.S + kKeyChunk - 1) / kKeyChunk;
-    const int64_t grid = nchunk * a.B * a.H;
-    if (grid > 0) hipLaunchKernelGGL(quantize_key_kernel<DT>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
-  } else {
-    const int64_t threads = a.B * a.H * a.S * (a.D / 32) * 4;
-    const int64_t grid = (threads + 255) / 256;
-    if (grid > 0) hipLaunchKernelGGL(quantize_hd_kernel<DT>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
-  }
-}
-
-hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
-  if (a.dtype == 0) launch_quantize_t<0>(a, stream);
-  else if (a.dtype == 1) launch_quantize_t<1>(a, stream);
-  else launch_quantize_t<2>(a, stream);
+// Jobs with the sequence-blocked layout go first: their workgroups have the
+// longer dependency chain (load, LDS, barrier, encode), so they should not
+// form the tail of the launch.
+hipError_t launch_quantize_batch(const QuantArgs* jobs, int n, hipStream_t stream) {
+  if (n < 1 || n > kMaxQuantJobs) return hipErrorInvalidValue;
+  QuantBatch p{};
+  int64_t total = 0;
+  int k = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int i = 0; i < n; ++i) {
+      const QuantArgs& a = jobs[i];
+      if ((a.key_layout != 0) != (pass == 0)) continue;
+      const int64_t gx = a.key_layout ? (a.S + kKeyChunk - 1) / kKeyChunk
+                                      : (a.S * (a.D / 32) + kHdBlocksPerGroup - 1) / kHdBlocksPerGroup;
+      p.job[k] = a;
+      p.gx[k] = static_cast<int>(gx);
+      p.start[k] = static_cast<int>(total);
+      total += gx * a.H * a.B;
+      if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+      ++k;
+    }
+  p.n = k;
+  p.start[k] = static_cast<int>(total);
+  if (total > 0) hipLaunchKernelGGL(quantize_kernel, dim3(static_cast<unsigned>(total)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -71,7 +71,9 @@ typedef enum { MXATTN_LAYOUT_HD = 0, MXATTN_LAYOUT_KEY = 1 } mxattn_layout_t;
  * Byte address of row r of (b, h):
  *   codes  + b*code_stride[0]  + h*code_stride[1]  + r*code_stride[2]
  *   scales + b*scale_stride[0] + h*scale_stride[1] + r*scale_stride[2]
- * where r is the token (HD) or the channel (KEY). */
+ * where r is the token (HD) or the channel (KEY).
+ * Every entry point rejects batch or heads above 65535 and seq above 2^26
+ * with MXATTN_ERR_UNSUPPORTED. */
 typedef struct {
   uint8_t* codes;
   uint8_t* scales;
@@ -102,6 +104,31 @@ typedef struct {
 mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
                                 const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
                                 const mxattn_mx_t* out, mxattn_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * mxattn_quantize_batch -- the same encoding as mxattn_quantize for up to
+ * MXATTN_MAX_QUANTIZE_JOBS tensors in one launch (for instance the Q, K and
+ * V of one attention call, which are too small to fill the device one at a
+ * time).  Each job carries exactly the arguments of mxattn_quantize, with
+ * the same meaning and checks; the results are bit-identical to calling
+ * mxattn_quantize once per job.  Jobs may differ in dtype, shape, layout and
+ * rule.  The outputs of different jobs must not overlap each other or any
+ * job's input (not checked; overlapping jobs give unspecified results).
+ * Errors: MXATTN_ERR_INVALID_ARG for a null list or n_jobs outside
+ * [1, MXATTN_MAX_QUANTIZE_JOBS]; otherwise the first failing job's error,
+ * with nothing launched. */
+#define MXATTN_MAX_QUANTIZE_JOBS 4
+typedef struct {
+  const void* x;
+  mxattn_dtype_t x_dtype;
+  int32_t reserved;
+  int64_t x_stride[3];
+  const float* chan_scale;
+  mxattn_scale_rule_t rule;
+  float qmax;
+  const mxattn_mx_t* out;
+} mxattn_quantize_job_t;
+mxattn_status_t mxattn_quantize_batch(const mxattn_quantize_job_t* jobs, int32_t n_jobs, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * mxattn_smooth_calibrate -- static per-channel Smooth-QK factors from a

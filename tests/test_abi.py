@@ -112,6 +112,33 @@ def test_quantize_rejects_without_launch():
     assert lib.mxattn_quantize(ctypes.c_void_p(65), 2, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
 
 
+def test_quantize_batch_rejects_without_launch():
+    lib = mxa.library()
+    outs = [_mx(), _mx(layout=1)]
+    jobs = (mxa._QuantJob * 5)()
+    for j in jobs:
+        j.x = 64
+        j.x_dtype = 2
+        j.x_stride[:] = [0, 0, 128]
+        j.rule = 0
+        j.qmax = 7.25
+        j.out = ctypes.pointer(outs[0])
+    assert lib.mxattn_quantize_batch(None, 1, None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize_batch(jobs, 0, None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize_batch(jobs, 5, None) == mxa.ERR_INVALID_ARG
+    # A bad later job stops the whole batch and is named in the message.
+    jobs[1].rule, jobs[1].qmax = 1, 8.5
+    assert lib.mxattn_quantize_batch(jobs, 2, None) == mxa.ERR_UNSUPPORTED
+    assert b"job[1]" in lib.mxattn_last_error()
+    jobs[1].rule, jobs[1].qmax = 0, 7.25
+    jobs[1].out = ctypes.pointer(outs[1])
+    jobs[1].x = 66
+    assert lib.mxattn_quantize_batch(jobs, 2, None) == mxa.ERR_INVALID_ARG
+    assert b"job[1]" in lib.mxattn_last_error()
+    jobs[0].out = None
+    assert lib.mxattn_quantize_batch(jobs, 1, None) == mxa.ERR_INVALID_ARG
+
+
 def test_calibrate_rejects():
     lib = mxa.library()
     f = ctypes.c_void_p(64)

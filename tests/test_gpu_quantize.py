@@ -109,6 +109,56 @@ def test_workload_shapes_q_k_v():
         assert_codes_equal(got, oc, os_, f"workload-2 {name}")
 
 
+def _batch_case(seed=21):
+    """Four jobs that differ in dtype, layout, rule, head_dim, sequence length
+    (ragged, and a single token) and input strides (a sliced, non-contiguous
+    view), two with channel factors."""
+    g = torch.Generator().manual_seed(seed)
+    base = (torch.randn((2, 5, 90, 128), generator=g) * 2).to(torch.bfloat16)
+    jobs = [
+        dict(x=base[:, 1:4, 3:80], layout="hd", chan_scale=torch.exp(torch.randn((3, 128), generator=g)), rule="ocp"),
+        dict(x=(torch.randn((1, 2, 100, 64), generator=g) * 5).to(torch.float16), layout="key",
+             chan_scale=torch.exp(torch.randn((2, 64), generator=g)), rule="uos"),
+        dict(x=torch.randn((3, 2, 1, 64), generator=g), layout="hd", rule="uos"),
+        dict(x=torch.randn((1, 1, 33, 128), generator=g).to(torch.bfloat16), layout="key", rule="ocp"),
+    ]
+    return jobs
+
+
+def test_quantize_batch_matches_oracle_and_single_calls():
+    jobs = _batch_case()
+    dev_jobs = [dict(j, x=j["x"].to(DEV), **({"chan_scale": j["chan_scale"].to(DEV)} if "chan_scale" in j else {}))
+                for j in jobs]
+    print("quantize_batch: 4 mixed jobs", flush=True)
+    got = mxa.quantize_batch(dev_jobs)
+    single = [mxa.quantize(**j) for j in dev_jobs]
+    torch.cuda.synchronize()
+    for i, (j, g1, s1) in enumerate(zip(jobs, got, single)):
+        assert torch.equal(g1.codes, s1.codes) and torch.equal(g1.scales, s1.scales), f"job {i}: batch != single"
+        x64 = host_f64(j["x"])
+        if "chan_scale" in j:
+            x64 = smooth.apply(x64.astype(np.float32), j["chan_scale"].numpy()).astype(np.float64)
+        r = mx.RULE_OCP if j["rule"] == "ocp" else mx.RULE_UOS
+        oc, os_ = oracle_quantize(x64, j["layout"], r)
+        assert_codes_equal(g1, oc, os_, f"batch job {i}")
+
+
+def test_quantize_batch_workload_q_k_v_with_smoothing():
+    """The prefill step's own call: Q and K with their Smooth-QK factors and
+    V in the key-blocked layout, one launch."""
+    d = synth.gqa_prefill(device=DEV, seq=512)
+    qs, ks = mxa.smooth_calibrate(d["q_cal"], d["k_cal"])
+    got = mxa.quantize_batch([dict(x=d["q"], chan_scale=qs), dict(x=d["k"], chan_scale=ks),
+                              dict(x=d["v"], layout="key")])
+    torch.cuda.synchronize()
+    for name, m, cs in (("q", got[0], qs), ("k", got[1], ks), ("v", got[2], None)):
+        x64 = host_f64(d[name])
+        if cs is not None:
+            x64 = smooth.apply(x64.astype(np.float32), cs.cpu().numpy()).astype(np.float64)
+        oc, os_ = oracle_quantize(x64, m.layout)
+        assert_codes_equal(m, oc, os_, f"batched workload {name}")
+
+
 def test_smooth_calibration_bit_exact():
     d = synth.gqa_prefill(device=DEV, seq=128)
     qs, ks = mxa.smooth_calibrate(d["q_cal"], d["k_cal"])
