@@ -62,6 +62,19 @@ __device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f c, int sa, int sb)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
 }
 
+// As mfma32_fp4, with the A scale taken from byte `sel` (0..3, a constant
+// after inlining) of the 32-bit word sa4 by the instruction's operand select.
+__device__ __forceinline__ v16f mfma32_fp4_sel(v4i a, v4i b, v16f c, int sa4, int sel, int sb) {
+  v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa4, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 1, sa4, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 2, sa4, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 3, sa4, 0, sb);
+  }
+}
+
 __device__ __forceinline__ v4f mfma16_fp4(v4i a, v4i b, v4f c, int sa, int sb) {
   v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
   v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};

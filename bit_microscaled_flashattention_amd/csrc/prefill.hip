@@ -46,12 +46,20 @@ struct Cfg {
   static constexpr int DT = D / 32;         // 32-channel tiles of O^T
   static constexpr int KRB = D / 2;         // bytes per K row (one key)
   static constexpr int VRB = BC / 2;        // bytes per V row (one channel, BC keys)
-  static constexpr int KSROW = D / 32;
-  static constexpr int VSROW = BC / 32;
+  static constexpr int KSROW = D / 32;        // K scale bytes per key
+  static constexpr int VSROW = BC / 32;       // V scale bytes per channel in a tile
+  // Scale bytes sit in LDS so that lane (row i, half hh) finds every byte
+  // one MFMA needs at a fixed position of one 32-bit word: word group g,
+  // half hh, row i is at g*256 + hh*128 + 4i.  K: group = kb / KPD, byte
+  // (kb % KPD)*DC + dc.  V: group = dt / DPD, byte (dt % DPD)*(KB/2) + pp.
+  static constexpr int KPD = 4 / DC;          // key blocks per K scale word
+  static constexpr int DPD = (KB / 2) >= 4 ? 1 : 4 / (KB / 2);  // channel tiles per V scale word
+  static constexpr int KS_BYTES = ((KB + KPD - 1) / KPD) * 256;
+  static constexpr int VS_BYTES = ((DT + DPD - 1) / DPD) * 256;
   static constexpr int OFF_V = BC * KRB;
   static constexpr int OFF_KS = OFF_V + D * VRB;
-  static constexpr int OFF_VS = OFF_KS + BC * KSROW;
-  static constexpr int STAGE = ((OFF_VS + D * VSROW) + 15) / 16 * 16;
+  static constexpr int OFF_VS = OFF_KS + KS_BYTES;
+  static constexpr int STAGE = ((OFF_VS + VS_BYTES) + 15) / 16 * 16;
   static constexpr int K_LOADS = BC * KRB / 1024;  // 1 KB direct-to-LDS wave loads per tile
   static constexpr int V_LOADS = D * VRB / 1024;
   static constexpr int NKS = BC * D / 32;          // K scale bytes per tile
@@ -164,15 +172,24 @@ __device__ __forceinline__ void issue_tile(const TileSrc& src, int t0, uint8_t* 
   }
 }
 
-// The scale bytes of one LDS scale row (2, 4 or 8 bytes) as a 64-bit word.
-template <int ROWBYTES>
-__device__ __forceinline__ uint64_t scale_row(const uint8_t* base, int row) {
-  if constexpr (ROWBYTES == 8) return *reinterpret_cast<const uint64_t*>(base + row * 8);
-  if constexpr (ROWBYTES == 4) return *reinterpret_cast<const uint32_t*>(base + row * 4);
-  return *reinterpret_cast<const uint16_t*>(base + row * 2);
+// LDS positions (inside a stage) of the scale bytes a thread fetched: K
+// byte e is (tile row r = e / KSROW, chunk c = e % KSROW), used by lane
+// (row r % 32, half c % 2) in the MFMA of key block r / 32 and 64-deep chunk
+// c / 2.  V byte e is (channel d = e / VSROW, key block k = e % VSROW), used
+// by lane (row d % 32, half k % 2) in the MFMA of channel tile d / 32 and
+// key-block pair k / 2.
+template <int D, int BC>
+__device__ __forceinline__ int ks_pos(int e) {
+  using C = Cfg<D, BC>;
+  const int r = e / C::KSROW, c = e % C::KSROW, kb = r / 32;
+  return C::OFF_KS + (kb / C::KPD) * 256 + (c % 2) * 128 + (r % 32) * 4 + (kb % C::KPD) * C::DC + c / 2;
 }
-
-__device__ __forceinline__ int scale_byte(uint64_t w, int i) { return static_cast<int>((w >> (8 * i)) & 0xFF); }
+template <int D, int BC>
+__device__ __forceinline__ int vs_pos(int e) {
+  using C = Cfg<D, BC>;
+  const int d = e / C::VSROW, k = e % C::VSROW, dt = d / 32;
+  return C::OFF_VS + (dt / C::DPD) * 256 + (k % 2) * 128 + (d % 32) * 4 + (dt % C::DPD) * (C::KB / 2) + k / 2;
+}
 
 template <int D, int BC>
 __device__ __forceinline__ void store_scales(const ScaleRegs<D, BC>& sr, uint8_t* stage, int tid) {
@@ -180,24 +197,28 @@ __device__ __forceinline__ void store_scales(const ScaleRegs<D, BC>& sr, uint8_t
 #pragma unroll
   for (int i = 0; i < C::IKS; ++i) {
     const int e = tid + kThreads * i;
-    if (e < C::NKS) stage[C::OFF_KS + e] = sr.ks[i];
+    if (e < C::NKS) stage[ks_pos<D, BC>(e)] = sr.ks[i];
   }
 #pragma unroll
   for (int i = 0; i < C::IVS; ++i) {
     const int e = tid + kThreads * i;
-    if (e < C::NVS) stage[C::OFF_VS + e] = sr.vs[i];
+    if (e < C::NVS) stage[vs_pos<D, BC>(e)] = sr.vs[i];
   }
 }
 
-// E8M0 byte of a P block maximum pmax in [0, 1]: floor(log2 pmax) - 2 (OCP),
-// one more when the significand exceeds thr (UOS), clamped below at 1 so the
-// convert's scale stays a normal float (zero and tiny maxima take byte 1;
-// their codes are 0 either way).  pmax <= 1 keeps the byte below 126.
-__device__ __forceinline__ int p_scale_byte(float pmax, int thr) {
+// E8M0 scale of a P block maximum pmax in [0, 1], as the float 2^(b-127):
+// b = floor(log2 pmax) - 2 (OCP), one more when the significand exceeds
+// thr (UOS), clamped below at 1 so the convert's scale stays a normal float
+// (zero and tiny maxima take byte 1; their codes are 0 either way).  In
+// floats: the power of two at or below pmax, times 1/4, times 2 under the
+// UOS condition, at least 2^-126.  Subnormal intermediates are kept (the
+// code is built without denormal flushing), so this equals the integer
+// rule exactly.  pmax <= 1 keeps the byte below 126.
+__device__ __forceinline__ float p_block_scale(float pmax, bool uos, int thr) {
   const uint32_t bits = __float_as_uint(pmax);
-  const int inc = static_cast<int>(bits & 0x7FFFFFu) > thr ? 1 : 0;
-  const int b = static_cast<int>(bits >> 23) - 2 + inc;
-  return b < 1 ? 1 : b;
+  float s = __uint_as_float(bits & 0x7F800000u) * 0.25f;
+  if (uos) s = static_cast<int>(bits & 0x7FFFFFu) > thr ? s * 2.0f : s;
+  return fmaxf(s, 0x1p-126f);
 }
 
 // Workgroup -> (query block, batch, query head).  Consecutive workgroups go
@@ -227,7 +248,7 @@ __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int
   hq = (pair % a.Hkv) * G + g;
 }
 
-template <int D, int BC, bool CAUSAL, bool LQ>
+template <int D, int BC, bool CAUSAL, bool LQ, bool PUOS>
 __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, BC>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
@@ -281,10 +302,10 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   for (int dc = 0; dc < C::DC; ++dc) koff[dc] = j * C::KRB + 16 * swz<C::KRB>(j, 2 * dc + hh);
 #pragma unroll
   for (int pp = 0; pp < C::KB / 2; ++pp) voff[pp] = C::OFF_V + j * C::VRB + 16 * swz<C::VRB>(j, 2 * pp + hh);
-  const int ksoff = C::OFF_KS + j * C::KSROW, vsoff = C::OFF_VS + j * C::VSROW;
-  // UOS threshold on the significand bits of a P block maximum (never met
-  // under the OCP rule): significand 1.m above qmax/4, qmax/4 in (1, 2).
-  const int p_thr = a.p_uos ? static_cast<int>(__float_as_uint(a.p_qmax_quarter) & 0x7FFFFFu) : 0x7FFFFFFF;
+  const int ksoff = C::OFF_KS + hh * 128 + j * 4, vsoff = C::OFF_VS + hh * 128 + j * 4;
+  // UOS (read only when PUOS): a P block maximum whose significand 1.m
+  // exceeds qmax/4, a value in (1, 2), takes the next scale up.
+  const int p_thr = static_cast<int>(__float_as_uint(a.p_qmax_quarter) & 0x7FFFFFu);
 
   float m = -__builtin_huge_valf();
   float lsum = 0.0f;  // baseline normaliser (sum of unquantised P~)
@@ -330,10 +351,11 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
           aop[dc] = *reinterpret_cast<const v4i*>(base + koff[dc] + kb * 32 * C::KRB);
-        const uint64_t ksw = scale_row<C::KSROW>(base + ksoff + kb * 32 * C::KSROW, 0);
+        const int ksw = *reinterpret_cast<const int*>(base + ksoff + (kb / C::KPD) * 256);
         v16f acc = v16f{};
 #pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc) acc = mfma32_fp4(aop[dc], qop[dc], acc, scale_byte(ksw, 2 * dc + hh), qsc[dc]);
+        for (int dc = 0; dc < C::DC; ++dc)
+          acc = mfma32_fp4_sel(aop[dc], qop[dc], acc, ksw, (kb % C::KPD) * C::DC + dc, qsc[dc]);
         if (blk_masked(kb)) {
           const int qlim = CAUSAL ? qrow : 0x7FFFFFFF;
 #pragma unroll
@@ -394,9 +416,8 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
           eb[h2] = 1;
           if (blk_empty(kb)) continue;
           v16f& p = S[kb];
-          const int byte = p_scale_byte(fast_exp2((bm[kb] - m_new) * a.c), p_thr);
-          eb[h2] = byte;
-          const float scl = scale_of_byte(byte);
+          const float scl = p_block_scale(fast_exp2((bm[kb] - m_new) * a.c), PUOS, p_thr);
+          eb[h2] = static_cast<int>(__float_as_uint(scl) >> 23);
 #pragma unroll
           for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(p[r], a.c, -mc));
           if constexpr (!LQ) {
@@ -406,7 +427,9 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts), __float_as_uint(ts), false, false);
             lsum += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
           }
-          uint32_t w0 = 0, w1 = 0;
+          uint32_t w0, w1;
+          asm("" : "=v"(w0));
+          asm("" : "=v"(w1));
           w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[0], p[1], scl, 0);
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[8], p[9], scl, 0);
           w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
@@ -428,10 +451,11 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           aop[dt] = *reinterpret_cast<const v4i*>(base + voff[pp] + dt * 32 * C::VRB);
-          sa[dt] = scale_byte(scale_row<C::VSROW>(base + vsoff + dt * 32 * C::VSROW, 0), 2 * pp + hh);
+          sa[dt] = *reinterpret_cast<const int*>(base + vsoff + (dt / C::DPD) * 256);
         }
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) O[dt] = mfma32_fp4(aop[dt], bop, O[dt], sa[dt], bsc);
+        for (int dt = 0; dt < C::DT; ++dt)
+          O[dt] = mfma32_fp4_sel(aop[dt], bop, O[dt], sa[dt], (dt % C::DPD) * (C::KB / 2) + pp, bsc);
         L = mfma16_fp4(ones, bop, L, a.one_scale, bsc);
       }
     };
@@ -481,18 +505,24 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
     }
 }
 
-template <int D, int BC>
-static void launch_t(const PrefillArgs& a, int causal, hipStream_t stream) {
+template <int D, int BC, bool PUOS>
+static void launch_tp(const PrefillArgs& a, int causal, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.n_qblk) * a.B * a.Hq;
   const bool lq = a.l_from_quantized != 0;
   if (causal && lq)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, true, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (causal)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, false, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (lq)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, false, true, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BC, false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, false, false, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
+}
+
+template <int D, int BC>
+static void launch_t(const PrefillArgs& a, int causal, hipStream_t stream) {
+  if (a.p_uos) launch_tp<D, BC, true>(a, causal, stream);
+  else launch_tp<D, BC, false>(a, causal, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream) {
