@@ -101,18 +101,26 @@ __device__ __forceinline__ void pv_chunk(DecState& st, const uint8_t* vr, int la
     for (int dt = 0; dt < 8; ++dt)
       if (dt * 16 < D) st.O[dt] *= alpha;
   }
+  // The A operand of lane (channel dl, group g) is the bf16 of tokens
+  // chunk_tok(g, 0..7) in channel 16 dt + dl, read with the LDS transpose
+  // load: in each 16-lane group, lane 4a + b receives element b of the
+  // 8-byte reads of lanes a, a + 4, a + 8, a + 12.  So lane s reads channels
+  // [16 dt + 4 (s % 4), +4) of token 4g + s / 4 (then 16 more tokens on).
+  const int s16 = lane & 15;
+  const uint8_t* vsrc = vr + (4 * g + (s16 >> 2)) * kVRow + 8 * (s16 & 3);
+  (void)dl;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     if (dt * 16 >= D) break;
-    const int d = dt * 16 + dl;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t a = *reinterpret_cast<const uint16_t*>(vr + chunk_tok(g, 2 * i) * kVRow + d * 2);
-      const uint32_t b = *reinterpret_cast<const uint16_t*>(vr + chunk_tok(g, 2 * i + 1) * kVRow + d * 2);
-      w[i] = a | (b << 16);
-    }
-    const v4i aop = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    lds_v4s* p0 = (lds_v4s*)(vsrc + 32 * dt);
+    lds_v4s* p1 = (lds_v4s*)(vsrc + 32 * dt + 16 * kVRow);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+    const v2i_t l2 = __builtin_bit_cast(v2i_t, lo), h2 = __builtin_bit_cast(v2i_t, hi);
+    const v4i aop = {l2[0], l2[1], h2[0], h2[1]};
     const v4f o = mfma16_bf16(aop, bhi, st.O[dt]);
     st.O[dt] = mfma16_bf16(aop, blo, o);
   }
