@@ -281,10 +281,6 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
   return after_launch(launch_prefill(a, static_cast<int>(q->dim), kv_tile, p->causal != 0, s), s, "prefill");
 }
 
-// Rows of the bf16 hybrid set handled per partial slot (one workgroup each).
-static constexpr int64_t kBf16Rows = 256;
-static constexpr int64_t kMaxSlots = 4096;
-
 static int64_t bf16_slots(int64_t hybrid_rows) { return hybrid_rows > 0 ? (hybrid_rows + kBf16Rows - 1) / kBf16Rows : 0; }
 
 size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int64_t dim, int64_t tcap,

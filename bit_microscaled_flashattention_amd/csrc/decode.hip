@@ -31,8 +31,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kDecThreads = 256;
 constexpr int kChunk = 32;          // tokens per wave iteration
 constexpr int kVRow = 256 + 16;     // LDS bytes per staged bf16 V row (128 ch + pad)
-constexpr int kBf16Rows = 256;      // bf16 hybrid rows per workgroup
-constexpr int kMaxSlots = 4096;     // partial slots per (batch, query head) the merge handles
 
 __device__ __forceinline__ v4f mfma16_bf16(v4i a, v4i b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
@@ -395,7 +393,6 @@ __device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, 
   auto row_v = [&](int i) -> const uint16_t* {
     return i < nsel ? a.v_sel + (bh * a.max_sel + i) * D : a.v_win + (bh * a.window + woff + (i - nsel)) * D;
   };
-  auto valid = [&](int i) -> bool { return i < r_end && (i >= nsel || idx[i] < limit); };
 
   DecState st;
   st.m = -__builtin_huge_valf();
@@ -403,35 +400,64 @@ __device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, 
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.O[dt] = v4f{0, 0, 0, 0};
 
-  // Wave w takes the chunks r_begin + 32 (w + 4 i).
-  for (int t0 = r_begin + wave * kChunk; t0 < r_end; t0 += 4 * kChunk) {
-    for (int e = lane; e < kChunk * (D / 8); e += 64) {
-      const int tt = e / (D / 8), part = e % (D / 8);
-      v4i x = {0, 0, 0, 0};
-      if (t0 + tt < r_end) x = *reinterpret_cast<const v4i*>(row_v(t0 + tt) + part * 8);
-      *reinterpret_cast<v4i*>(vr + tt * kVRow + part * 16) = x;
+  // Wave w takes the chunks r_begin + 32 (w + 4 i).  A chunk's row loads are
+  // all issued together, and the next chunk's are issued as soon as this
+  // chunk's rows have gone to LDS and into its QK^T products, so they land
+  // during this chunk's softmax and PV.  Rows past r_end read row r_end - 1
+  // (finite values that only meet P = 0 or a masked score).
+  constexpr int kParts = D / 8;                     // 16-byte pieces per bf16 row
+  constexpr int kVIter = kChunk * kParts / 64;      // V pieces per lane
+  v4i vx[kVIter];
+  v4i kx[2][4];
+  bool ok_row = false;
+  auto load_chunk = [&](int t0) {
+    ok_row = false;
+    if (lane < kChunk && t0 + lane < r_end) ok_row = t0 + lane >= nsel || idx[t0 + lane] < limit;
+#pragma unroll
+    for (int it = 0; it < kVIter; ++it) {
+      const int e = lane + 64 * it;
+      const int tt = e / kParts, part = e % kParts;
+      const int i = min(t0 + tt, r_end - 1);
+      vx[it] = *reinterpret_cast<const v4i*>(row_v(i) + part * 8);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = min(t0 + h * 16 + j, r_end - 1);
+      const uint16_t* kr = row_k(i);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kx[h][kk] = kk * 32 < D ? *reinterpret_cast<const v4i*>(kr + kk * 32 + 8 * g) : v4i{0, 0, 0, 0};
+    }
+  };
+  int t0 = r_begin + wave * kChunk;
+  if (t0 < r_end) load_chunk(t0);
+  for (; t0 < r_end; t0 += 4 * kChunk) {
+    // Validity of the chunk's rows as a bit mask: lane i < 32 tested row t0 + i.
+    const uint32_t vmask = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(ok_row));
+#pragma unroll
+    for (int it = 0; it < kVIter; ++it) {
+      const int e = lane + 64 * it;
+      const int tt = e / kParts, part = e % kParts;
+      *reinterpret_cast<v4i*>(vr + tt * kVRow + part * 16) = vx[it];
     }
     v4f sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int i = t0 + h * 16 + j;
-      const bool ok = i < r_end;
-      const uint16_t* kr = ok ? row_k(i) : nullptr;
       v4f acc = {0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk * 32 >= D) break;
-        const v4i aop = ok ? *reinterpret_cast<const v4i*>(kr + kk * 32 + 8 * g) : v4i{0, 0, 0, 0};
-        acc = mfma16_bf16(aop, qop[kk], acc);
+        acc = mfma16_bf16(kx[h][kk], qop[kk], acc);
       }
       sc[h] = acc;
     }
+    if (t0 + 4 * kChunk < r_end) load_chunk(t0 + 4 * kChunk);
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tk = chunk_tok(g, i);
       const float x = i < 4 ? sc[0][i] : sc[1][i - 4];
-      sv[i] = (valid(t0 + tk) && j < G) ? x : -__builtin_huge_valf();
+      sv[i] = (((vmask >> tk) & 1u) && j < G) ? x : -__builtin_huge_valf();
     }
     v4i bhi, blo;
     float alpha;
@@ -439,6 +465,8 @@ __device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, 
     softmax_chunk(st, sv, a.c, bhi, blo, alpha, moved);
     wave_lds_sync();
     pv_chunk(st, vr, lane, bhi, blo, alpha, moved, D);
+    // The next chunk's rows overwrite this wave's staging rows.
+    wave_lds_sync();
   }
   __syncthreads();
   combine_store<D>(vstage, st, a, b, hk, a.n_split + part_id, a.n_split + a.n_bf16);

@@ -22,6 +22,11 @@ struct QuantArgs {
   int64_t ss[3];
 };
 
+// bf16 hybrid rows per decode workgroup (one partial slot each), and the
+// partial slots per (sequence, query head) the decode merge accepts.
+constexpr int kBf16Rows = 256;
+constexpr int kMaxSlots = 4096;
+
 // Up to kMaxQuantJobs tensors quantised by one launch; start[i] is the first
 // workgroup of job i and start[n] the grid size, gx[i] the workgroups along
 // the sequence of one (batch, head) of job i.
