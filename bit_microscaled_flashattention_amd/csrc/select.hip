@@ -280,7 +280,11 @@ __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs 
     const KBlock<D> kb = kn;
     kn = load_kblock<D>(rc, rs, kcs, kss, t0 + 128 + j, k_hi, hh);
     float colsum = 0.0f;
-    for (int g = 0; g < ng; ++g) {
+    // Unrolled over the largest group count with a uniform skip, so the next
+    // group's MFMAs can issue while this group's exponentials run.
+#pragma unroll
+    for (int g = 0; g < kStatGroups; ++g) {
+      if (g >= ng) continue;
       // A operand: queries g*32 + (lane % 32) from LDS.
       const int qa = g * 32 + j;
       v16f s = v16f{};
