@@ -54,7 +54,7 @@ typedef enum { MXATTN_F32 = 0, MXATTN_F16 = 1, MXATTN_BF16 = 2 } mxattn_dtype_t;
 /* E8M0 scale rule of a block with maximum magnitude amax:
  *   OCP: e = floor(log2 amax) - 2          (amax / 2^e in [4, 8))
  *   UOS: smallest e with amax <= qmax*2^e  (amax / 2^e in (qmax/2, qmax]),
- *        qmax in (4, 8); the pages' value is 7.25.
+ *        qmax in (4, 8); MXAttention (Abstract) uses 7.25.
  * e is clamped to [-127, 127]; an all-zero block gets e = -127 (byte 0). */
 typedef enum { MXATTN_SCALE_OCP = 0, MXATTN_SCALE_UOS = 1 } mxattn_scale_rule_t;
 

@@ -22,7 +22,7 @@ The operands handed to these functions are already-dequantised float64
 arrays (q_hat, k_hat, v_hat).  Quantisation of Q, K, V is done separately with
 oracle.mx so that each step can be checked on its own.
 
-Readings (listed in DESIGN.md)
+Readings
   * softmax_scale (1/sqrt(D) by default) multiplies the logits after the
     product; it is not folded into Q before quantisation.
   * Keys are visited in tiles of Bc = kv_tile keys in ascending order.  The
@@ -36,7 +36,7 @@ Readings (listed in DESIGN.md)
   * Causal masking (Sq == Sk only): key t is visible to query i iff t <= i.
   * l_from_quantized=True is the PNQ / P-Reordering normaliser (l = sum P_hat);
     False is the baseline that sums the unquantised exponentials.
-  * Decode does not quantise P (the pages give no decode P format; the
+  * Decode does not quantise P (none of the sources gives a decode P format; the
     cache's V blocks run along head_dim, so a 4-bit PV contraction over keys
     has no block scales to use).
 
@@ -47,7 +47,7 @@ the effective weights are non-negative and sum to one per row; l >= 1; the
 smoothing rescale is output-neutral; decode equals the prefill path on the
 same operands; hybrid decode reduces to pure-FP4 and to pure-BF16 attention
 in its two limits.  Attention values under quantisation have no worked
-example on the pages: beyond those invariants they are "parity unpinned".
+example in the sources: beyond those invariants they are "parity unpinned".
 """
 
 import numpy as np

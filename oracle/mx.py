@@ -14,7 +14,7 @@ bound of "MXAttention: Data-Free Optimal Scaling and Pre-Normalization
 Quantization for MXFP4 Attention" (Abstract, AI Summary): a fixed boundary
 Qmax = 7.25 on the block maximum measured in scale units.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the sources are silent:
   * E2M1 rounding is round-to-nearest, ties to the code whose mantissa bit is
     0; magnitudes above 6 saturate to 6; there is no Inf/NaN code.
   * A value that rounds to zero keeps its sign bit (code 0x8 for -0).

@@ -9,7 +9,7 @@ column mass; the top-rho fraction (5% by default) is taken from the
 non-window prefix; the window size is fixed; identification is a light
 reduction run every 64 tokens.
 
-Readings (listed in DESIGN.md)
+Readings
   * Column mass of key t gains, for every recent query r (at most 64, the
     queries decoded since the last selection) and every query head of the KV
     head's group, the softmax probability of t among all keys t' < ctx,

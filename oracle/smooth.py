@@ -10,7 +10,7 @@ BitDecoding-FP4 page ("Outlier-Aware Key Quantization") describes the same
 static smoothing: per-channel coefficients estimated in a calibration phase,
 keys rescaled per channel.
 
-Readings (listed in DESIGN.md):
+Readings:
   * SmoothQuant form with strength 1/2: for KV head h and channel c,
         s = sqrt(kmax[h, c] / qmax[h, c])
     where kmax is max |K| over the calibration tokens and qmax is max |Q| over

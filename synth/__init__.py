@@ -5,10 +5,12 @@ attention or quantisation arithmetic.  Both the HIP path (through the tests
 and the benchmark) and the CPU oracle receive exactly these tensors.
 
 Every tensor comes from its own ``torch.Generator`` seeded with
-``1000 * workload + tensor_id`` (ids: Q 1, K 2, V 3, calibration 4,
-structure 5, recent queries 6).  Values are drawn in float32 and rounded to
-bfloat16/float16 by torch's round-to-nearest-even cast.  The stream of a
-generator depends on the device it lives on, so a workload generated on the
+``1000 * stream + tensor_id``, where ``stream`` is a fixed id per generator
+function (tiny 1, gqa_prefill 2, long_decode 3, hybrid_decode 4,
+diffusion 5) and the tensor ids are Q 1, K 2, V 3, calibration 4,
+structure 5, recent queries 6.  Values are drawn in float32 and rounded to
+bfloat16/float16 by torch's round-to-nearest-even cast.  The numbers a
+generator produces depend on the device it lives on, so a workload generated on the
 GPU is copied back to the host before the oracle sees it (never regenerated
 on the CPU).
 """
@@ -20,8 +22,8 @@ import torch
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_CAL, TENSOR_STRUCT, TENSOR_RECENT = 1, 2, 3, 4, 5, 6
 
 
-def seed_of(workload, tensor_id):
-    return 1000 * int(workload) + int(tensor_id)
+def seed_of(stream, tensor_id):
+    return 1000 * int(stream) + int(tensor_id)
 
 
 def _gen(device, seed):
@@ -38,7 +40,7 @@ def randn(shape, seed, device="cpu", dtype=torch.bfloat16, scale=1.0):
     return x.to(dtype)
 
 
-# ---------------------------------------------------------------- workload 1
+# ---------------------------------------- tiny non-causal prefill
 def tiny(device="cpu", seq=128, head_dim=64, seed_base=1):
     """Batch 1, one head, fp16 Q/K/V ~ N(0, 1)."""
     shp = (1, 1, seq, head_dim)
@@ -49,13 +51,13 @@ def tiny(device="cpu", seq=128, head_dim=64, seed_base=1):
     }
 
 
-# ---------------------------------------------------------------- workload 2
+# ------------------------------------------ 4K causal GQA prefill
 def gqa_prefill(device="cpu", batch=1, hq=32, hkv=8, seq=4096, head_dim=128,
-                n_outlier=4, outlier_gain=12.0, cal_tokens=256, workload=2):
+                n_outlier=4, outlier_gain=12.0, cal_tokens=256, stream=2):
     """bf16 N(0,1) Q/K/V; per KV head ``n_outlier`` K channels (seeded choice
     without replacement) multiplied by ``outlier_gain``; a separate calibration
     slice of ``cal_tokens`` tokens drawn the same way."""
-    gs = _gen("cpu", seed_of(workload, TENSOR_STRUCT))
+    gs = _gen("cpu", seed_of(stream, TENSOR_STRUCT))
     chans = torch.stack([torch.randperm(head_dim, generator=gs)[:n_outlier] for _ in range(hkv)])
     gain = torch.ones(hkv, head_dim)
     gain.scatter_(1, chans, outlier_gain)
@@ -66,28 +68,28 @@ def gqa_prefill(device="cpu", batch=1, hq=32, hkv=8, seq=4096, head_dim=128,
         x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
         return (x * gain).to(torch.bfloat16)
 
-    q = randn((batch, hq, seq, head_dim), seed_of(workload, TENSOR_Q), device)
-    k = make_k((batch, hkv, seq, head_dim), seed_of(workload, TENSOR_K))
-    v = randn((batch, hkv, seq, head_dim), seed_of(workload, TENSOR_V), device)
-    gc = _gen(device, seed_of(workload, TENSOR_CAL))
+    q = randn((batch, hq, seq, head_dim), seed_of(stream, TENSOR_Q), device)
+    k = make_k((batch, hkv, seq, head_dim), seed_of(stream, TENSOR_K))
+    v = randn((batch, hkv, seq, head_dim), seed_of(stream, TENSOR_V), device)
+    gc = _gen(device, seed_of(stream, TENSOR_CAL))
     q_cal = torch.randn((hq, cal_tokens, head_dim), generator=gc, device=device).to(torch.bfloat16)
     k_cal = (torch.randn((1, hkv, cal_tokens, head_dim), generator=gc, device=device)
              * gain).to(torch.bfloat16)[0]
     return {"q": q, "k": k, "v": v, "q_cal": q_cal, "k_cal": k_cal, "outlier_channels": chans}
 
 
-# ---------------------------------------------------------------- workload 3
-def long_decode(device="cpu", batch=32, hq=32, hkv=8, ctx=32768, head_dim=128, workload=3):
+# ------------------------------------------- 32K decode, batch 32
+def long_decode(device="cpu", batch=32, hq=32, hkv=8, ctx=32768, head_dim=128, stream=3):
     """bf16 N(0,1) keys/values for the cache and one N(0,1) query per head."""
     return {
-        "q": randn((batch, hq, head_dim), seed_of(workload, TENSOR_Q), device),
-        "k": randn((batch, hkv, ctx, head_dim), seed_of(workload, TENSOR_K), device),
-        "v": randn((batch, hkv, ctx, head_dim), seed_of(workload, TENSOR_V), device),
+        "q": randn((batch, hq, head_dim), seed_of(stream, TENSOR_Q), device),
+        "k": randn((batch, hkv, ctx, head_dim), seed_of(stream, TENSOR_K), device),
+        "v": randn((batch, hkv, ctx, head_dim), seed_of(stream, TENSOR_V), device),
         "ctx_len": torch.full((batch,), ctx, dtype=torch.int32, device=device),
     }
 
 
-# ---------------------------------------------------------------- workload 4
+# ------------------------------------- 32K hybrid decode, batch 8
 # Chosen so that the heaviest 5% of the non-window keys carry about 60% of the
 # attention mass of the recent queries (mean over the KV heads; the HyQuant
 # page reports 54-64% for real models).  Checked by tests/test_synth.py.
@@ -97,7 +99,7 @@ PARETO_SHAPE = 1.5
 
 
 def hybrid_decode(device="cpu", batch=8, hq=32, hkv=8, ctx=32768, head_dim=128,
-                  recent=64, gamma=HYBRID_GAMMA, beta=HYBRID_BETA, workload=4):
+                  recent=64, gamma=HYBRID_GAMMA, beta=HYBRID_BETA, stream=4):
     """bf16 N(0,1) keys/values/queries with a heavy-tailed column bias.
 
     Per (batch, KV head) a seeded unit vector u; every key gets
@@ -105,21 +107,21 @@ def hybrid_decode(device="cpu", batch=8, hq=32, hkv=8, ctx=32768, head_dim=128,
     every query (current and recent) gets beta * u, so a few keys dominate the
     attention of all queries of that KV head, as vertical lines do.
     """
-    gs = _gen(device, seed_of(workload, TENSOR_STRUCT))
+    gs = _gen(device, seed_of(stream, TENSOR_STRUCT))
     u = torch.randn((batch, hkv, head_dim), generator=gs, device=device)
     u = u / u.norm(dim=-1, keepdim=True)
     unif = torch.rand((batch, hkv, ctx), generator=gs, device=device)
     z = (1.0 - unif).clamp_min(1e-12).pow(-1.0 / PARETO_SHAPE)
-    gk = _gen(device, seed_of(workload, TENSOR_K))
+    gk = _gen(device, seed_of(stream, TENSOR_K))
     k = torch.randn((batch, hkv, ctx, head_dim), generator=gk, device=device)
     k = (k + gamma * z[..., None] * u[:, :, None, :]).to(torch.bfloat16)
     del z, unif
-    v = randn((batch, hkv, ctx, head_dim), seed_of(workload, TENSOR_V), device)
+    v = randn((batch, hkv, ctx, head_dim), seed_of(stream, TENSOR_V), device)
     g = hq // hkv
     ug = u.repeat_interleave(g, dim=1)                       # [B, Hq, D]
-    gq = _gen(device, seed_of(workload, TENSOR_Q))
+    gq = _gen(device, seed_of(stream, TENSOR_Q))
     q = (torch.randn((batch, hq, head_dim), generator=gq, device=device) + beta * ug)
-    gr = _gen(device, seed_of(workload, TENSOR_RECENT))
+    gr = _gen(device, seed_of(stream, TENSOR_RECENT))
     qr = (torch.randn((batch, hq, recent, head_dim), generator=gr, device=device)
           + beta * ug[:, :, None, :])
     return {
@@ -128,15 +130,15 @@ def hybrid_decode(device="cpu", batch=8, hq=32, hkv=8, ctx=32768, head_dim=128,
     }
 
 
-# ---------------------------------------------------------------- workload 5
+# ---------------------------------------- video-diffusion prefill
 def diffusion(device="cpu", batch=1, heads=24, frames=8, height=64, width=64,
-              head_dim=128, n_modes=16, lam=0.5, workload=5):
+              head_dim=128, n_modes=16, lam=0.5, stream=5):
     """bf16 Q/K/V = sqrt(1-lam) Z + sqrt(lam) F W: Z ~ N(0,1); tokens on a
     frames x height x width grid; F holds ``n_modes`` seeded low-frequency
     Fourier modes over the grid (unit variance); W ~ N(0, 1/n_modes) per head
     and per tensor."""
     seq = frames * height * width
-    gs = _gen("cpu", seed_of(workload, TENSOR_STRUCT))
+    gs = _gen("cpu", seed_of(stream, TENSOR_STRUCT))
     ft = torch.randint(0, 3, (n_modes,), generator=gs).float()
     fh = torch.randint(0, 5, (n_modes,), generator=gs).float()
     fw = torch.randint(0, 5, (n_modes,), generator=gs).float()
@@ -148,7 +150,7 @@ def diffusion(device="cpu", batch=1, heads=24, frames=8, height=64, width=64,
     modes = (math.sqrt(2.0) * torch.cos(arg)).to(device)          # [S, n_modes]
     out = {}
     for name, tid in (("q", TENSOR_Q), ("k", TENSOR_K), ("v", TENSOR_V)):
-        g = _gen(device, seed_of(workload, tid))
+        g = _gen(device, seed_of(stream, tid))
         zz = torch.randn((batch, heads, seq, head_dim), generator=g, device=device)
         w = torch.randn((heads, n_modes, head_dim), generator=g, device=device) / math.sqrt(n_modes)
         low = torch.matmul(modes, w)[None]          # [1, H, S, D]

@@ -161,11 +161,11 @@ def test_hybrid_decode_small(window, n_sel):
         assert (plain - out).abs().max().item() < 1e-5
 
 
-def test_decode_workload_3_full_size():
+def test_decode_32k_batch32_full_size():
     """Batch 32, 32/8 heads, D=128, ctx 32768, split 2048: cache codes of the
     sampled KV heads bit-exact, 12 sampled (b, hq) outputs vs the oracle."""
     d = synth.long_decode(device=DEV)
-    print("decode workload-3 full", flush=True)
+    print("decode 32K batch 32 full size", flush=True)
     kc, vc = _cache(d["k"], d["v"])
     qh = _query(d["q"])
     out, lse = mxa.decode(qh, kc, vc, d["ctx_len"], split_len=2048, return_lse=True)
@@ -178,14 +178,14 @@ def test_decode_workload_3_full_size():
         sub = mxa.MX(kc.codes[b:b + 1, kv:kv + 1], kc.scales[b:b + 1, kv:kv + 1], (1, 1, 32768, 128), "hd")
         assert_codes_equal(sub, *oc, f"cache b{b} kv{kv}")
     ref = _oracle_pair(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), pairs)
-    _compare(out, lse, ref, "workload-3")
+    _compare(out, lse, ref, "decode 32K batch 32")
 
 
-def test_hybrid_decode_workload_4_full_size():
+def test_hybrid_decode_32k_batch8_full_size():
     """Batch 8, 32/8 heads, ctx 32768, heavy-tailed column bias, window 128,
     1632 selected tokens per KV head (seeded), rest MXFP4."""
     d = synth.hybrid_decode(device=DEV)
-    print("hybrid decode workload-4 full", flush=True)
+    print("hybrid decode 32K batch 8 full size", flush=True)
     kc, vc = _cache(d["k"], d["v"])
     qh = _query(d["q"])
     hy, sets = _hybrid_inputs(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), 128, 1632, 1632, 9)
@@ -195,7 +195,7 @@ def test_hybrid_decode_workload_4_full_size():
     rng = np.random.default_rng(4)
     pairs = [(int(rng.integers(8)), int(rng.integers(32))) for _ in range(8)]
     ref = _oracle_pair(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), pairs, hybrid_sets=sets, q_bf=d["q"])
-    _compare(out, lse, ref, "workload-4 hybrid")
+    _compare(out, lse, ref, "hybrid 32K batch 8")
 
 
 # ------------------------------------------------------------------ selection
@@ -236,11 +236,11 @@ def _check_selection(gpu_idx, gpu_n, oracle_cm, ctx, window, num, den, what):
     assert all(cm[t] >= tau - eps for t in got), f"{what}: a clearly lighter token was selected"
 
 
-def test_select_vertical_workload_4():
+def test_select_vertical_32k_batch8():
     """col_mass from 64 recent queries x 4 heads per KV head over ctx 32768,
     then the top 5% of the non-window prefix; two calls accumulate."""
     d = synth.hybrid_decode(device=DEV)
-    print("select workload-4 full", flush=True)
+    print("select 32K batch 8 full size", flush=True)
     kc = mxa.quantize(d["k"], "hd")
     qr = mxa.quantize(d["q_recent"], "hd")
     col = torch.zeros((8, 8, 32768), dtype=torch.float32, device=DEV)

@@ -74,10 +74,10 @@ def _run_case(q, k, v, *, causal, kv_tile=128, p_rule="ocp", qkv_rule="ocp", l_f
     return worst
 
 
-def test_tiny_workload_1():
+def test_tiny_noncausal_128x64():
     """Batch 1, 1 head, S=128, D=64, fp16, non-causal, single key tile."""
     d = synth.tiny(device=DEV)
-    _run_case(d["q"], d["k"], d["v"], causal=False, what="workload-1")
+    _run_case(d["q"], d["k"], d["v"], causal=False, what="tiny 128x64")
 
 
 @pytest.mark.parametrize("kv_tile", [64, 128, 256])
@@ -135,7 +135,7 @@ def _sample_rows(seq, n, seed, heads):
             for h in heads}
 
 
-def test_workload_2_full_size_sampled_rows():
+def test_gqa_prefill_4k_causal_sampled_rows():
     """Causal GQA 32/8 heads, S=4096, D=128, outlier K channels, static
     Smooth-QK from the calibration slice; all codes compared, 24 sampled rows
     per head compared with the oracle."""
@@ -143,17 +143,17 @@ def test_workload_2_full_size_sampled_rows():
     qs, ks = mxa.smooth_calibrate(d["q_cal"], d["k_cal"])
     rows = _sample_rows(4096, 20, 5, range(32))
     _run_case(d["q"], d["k"], d["v"], causal=True, rows=rows, q_scale=qs, k_scale=ks,
-              what="workload-2 full")
+              what="4K causal GQA full size")
 
 
-def test_workload_5_sampled_rows():
+def test_diffusion_prefill_sampled_rows():
     """Non-causal, 24 heads, S=32768, UOS on Q, K, V and P: all heads run,
     three heads and ten rows each are compared with the oracle."""
     d = synth.diffusion(device=DEV)
     heads = [0, 7, 23]
     rows = _sample_rows(32768, 6, 6, heads)
     _run_case(d["q"], d["k"], d["v"], causal=False, p_rule="uos", qkv_rule="uos", rows=rows,
-              heads=heads, what="workload-5 full")
+              heads=heads, what="video diffusion full size")
 
 
 def test_deterministic_and_launch_order_independent():

@@ -106,7 +106,7 @@ def test_workload_shapes_q_k_v():
         got = mxa.quantize(d[name], layout=layout)
         torch.cuda.synchronize()
         oc, os_ = oracle_quantize(host_f64(d[name]), layout)
-        assert_codes_equal(got, oc, os_, f"workload-2 {name}")
+        assert_codes_equal(got, oc, os_, f"4K GQA prefill {name}")
 
 
 def _batch_case(seed=21):

@@ -8,7 +8,7 @@ import synth
 from oracle import mx, select
 
 
-def test_outlier_channels_of_workload_2():
+def test_outlier_channels_of_gqa_prefill():
     d = synth.gqa_prefill(device="cpu", seq=512)
     k = d["k"].float()[0]                                   # [Hkv, S, D]
     std = k.std(dim=1)                                      # [Hkv, D]
@@ -20,7 +20,7 @@ def test_outlier_channels_of_workload_2():
     assert d["q_cal"].shape == (32, 256, 128) and d["k_cal"].shape == (8, 256, 128)
 
 
-def test_workload_4_vertical_line_mass():
+def test_hybrid_decode_vertical_line_mass():
     """Top 5% of the non-window keys hold 50-70% of the recent queries' mass
     (mean over KV heads), computed by the oracle on the MXFP4 operands."""
     d = synth.hybrid_decode(device="cpu", batch=1)
@@ -36,7 +36,7 @@ def test_workload_4_vertical_line_mass():
     assert 0.5 <= np.mean(fracs) <= 0.7, fracs
 
 
-def test_workload_5_low_rank_structure():
+def test_diffusion_low_rank_structure():
     d = synth.diffusion(device="cpu", heads=2, frames=2, height=16, width=16)
     q = d["q"].float()[0, 0]                                 # [S, D]
     # The shared low-frequency part makes neighbouring tokens correlated;
