@@ -38,8 +38,8 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 PROFILED_TRAFFIC = {
     # fetch 7064 KiB x 2.000 + write 65831 KiB x 1.000 per dispatch
     "prefill_kernel<128,128,true,true>": {"bytes": 81877696, "sources": "e508824ecd3b825b"},
-    # fetch 557410 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch
-    "decode_scan_kernel<128> split 4096": {"bytes": 1146031424, "sources": "e39936271096051f"},
+    # fetch 557398 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch
+    "decode_scan_kernel<128> split 4096": {"bytes": 1146006976, "sources": "dbb9d526b2e62268"},
 }
 TRAFFIC_SOURCES = {
     "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
