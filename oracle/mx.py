@@ -150,6 +150,27 @@ def dequantize(codes, scale_bytes, axis, n=None):
     return np.moveaxis(v, -1, axis)
 
 
+def quantize_dual(x, axis, rule=RULE_OCP, qmax=UOS_QMAX):
+    """Dual-residual MXFP4: ``x`` ~ dequant(q1) + dequant(q2).
+
+    Source: BitDecoding-FP4, section "Dual-Residual Query Quantization": the
+    query is split into two FP4 tensors so that more of it survives than in
+    one, at no extra cache storage (only the query is split).  Reading (the
+    page does not print the split): q1 = MXFP4(x) and q2 = MXFP4(x -
+    dequant(q1)), both with the same block axis and scale rule.  The residual
+    is exact here (float64) and also in float32, because dequant(q1) is 0 or
+    within a factor of two of x (Sterbenz), so an fp32 implementation forms
+    the same residual bit for bit.
+    Returns (codes1, scales1, codes2, scales2) as :func:`quantize`.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[axis]
+    c1, s1 = quantize(x, axis, rule, qmax)
+    r = x - dequantize(c1, s1, axis, n)
+    c2, s2 = quantize(r, axis, rule, qmax)
+    return c1, s1, c2, s2
+
+
 def pack_nibbles(codes, axis=-1):
     """Two codes per byte along ``axis``: element 2j low nibble, 2j+1 high."""
     c = np.moveaxis(np.asarray(codes, dtype=np.uint8), axis, -1)
