@@ -86,7 +86,8 @@ def _load():
         "mxattn_quantize_batch": [P(_QuantJob), i32, vp],
         "mxattn_smooth_calibrate": [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp],
         "mxattn_prefill": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), vp, i32, vp, vp],
-        "mxattn_decode": [P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
+        "mxattn_decode": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
+        "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, P(_Mx), P(_Mx), vp],
         "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
     }
     for name, args in sig.items():
@@ -109,7 +110,7 @@ _lib = _load()
 
 # Every symbol the C header declares (checked by the CPU tests).
 EXPORTS = (
-    "mxattn_quantize", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
+    "mxattn_quantize", "mxattn_quantize_dual", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
     "mxattn_decode_workspace_bytes", "mxattn_decode",
     "mxattn_select_workspace_bytes", "mxattn_select_vertical",
     "mxattn_status_string", "mxattn_last_error", "mxattn_version",
@@ -198,6 +199,22 @@ def quantize(x, layout="hd", chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=Non
     return out
 
 
+def quantize_dual(x, chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None, out_res=None):
+    """Dual-residual MXFP4 of x [B,H,S,D] (HD blocks): returns (q1, q2) with
+    q1 = quantize(x) and q2 the MXFP4 of x - dequant(q1)."""
+    assert x.dim() == 4 and x.stride(3) == 1, "x must be [B,H,S,D] with contiguous D"
+    if out is None:
+        out = empty_mx(tuple(x.shape), "hd", x.device)
+    if out_res is None:
+        out_res = empty_mx(tuple(x.shape), "hd", x.device)
+    strides = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    cs = chan_scale.to(torch.float32).contiguous() if chan_scale is not None else None
+    d1, d2 = out.desc(), out_res.desc()
+    _check(_lib.mxattn_quantize_dual(_ptr(x), _DT[x.dtype], strides, _ptr(cs), _RULES[rule], float(qmax),
+                                     ctypes.byref(d1), ctypes.byref(d2), _stream(x)))
+    return out, out_res
+
+
 def quantize_batch(jobs):
     """Several quantize() calls in one launch.  jobs: list of dicts with the
     keyword arguments of quantize() (x required; layout, chan_scale, rule,
@@ -263,11 +280,12 @@ def decode_workspace_bytes(batch, hq, hkv, dim, tcap, split_len, hybrid_rows=0):
 
 
 def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybrid=None,
-           q_bf16=None, workspace=None, return_lse=False, out=None):
+           q_bf16=None, workspace=None, return_lse=False, out=None, q_res=None):
     """One query token per sequence against an MXFP4 KV cache.
 
     q: MX [B,Hq,1,D]; caches: MX [B,Hkv,Tcap,D]; ctx_len int32 [B] on device.
     hybrid: None or dict(idx, n_sel, k_sel, v_sel, k_win, v_win, window).
+    q_res: None or the residual MX of a dual-residual query (quantize_dual).
     """
     b, hq, _, d = q.shape
     hkv, tcap = k_cache.shape[1], k_cache.shape[2]
@@ -289,7 +307,9 @@ def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybr
         hy.k_win = hybrid["k_win"].data_ptr() if hybrid.get("k_win") is not None else None
         hy.v_win = hybrid["v_win"].data_ptr() if hybrid.get("v_win") is not None else None
     dq, dk, dv = q.desc(), k_cache.desc(), v_cache.desc()
-    _check(_lib.mxattn_decode(ctypes.byref(dq), _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv),
+    dqr = q_res.desc() if q_res is not None else None
+    _check(_lib.mxattn_decode(ctypes.byref(dq), ctypes.byref(dqr) if dqr is not None else None,
+                              _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv),
                               _ptr(ctx_len), ctypes.byref(hy) if hy is not None else None,
                               float(softmax_scale), int(split_len), _ptr(workspace), workspace.numel(),
                               _ptr(out), _ptr(lse), _stream(q.codes)))

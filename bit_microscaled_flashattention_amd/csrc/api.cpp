@@ -185,6 +185,29 @@ mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int
   return after_launch(launch_quantize_batch(&a, 1, s), s, "quantize");
 }
 
+mxattn_status_t mxattn_quantize_dual(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
+                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                     const mxattn_mx_t* out, const mxattn_mx_t* out_res, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("quantize_dual", &st)) return st;
+  QuantArgs a;
+  if ((st = quantize_args(x, x_dtype, x_stride, chan_scale, rule, qmax, out, "quantize_dual", &a)) != MXATTN_OK)
+    return st;
+  if (out->layout != MXATTN_LAYOUT_HD) return fail(MXATTN_ERR_UNSUPPORTED, "quantize_dual: out must use the HD layout");
+  if ((st = check_mx(out_res, "quantize_dual.out_res", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  if (out_res->batch != out->batch || out_res->heads != out->heads || out_res->seq != out->seq ||
+      out_res->dim != out->dim)
+    return fail(MXATTN_ERR_INVALID_ARG, "quantize_dual: out and out_res shapes differ");
+  a.codes2 = out_res->codes;
+  a.scales2 = out_res->scales;
+  for (int i = 0; i < 3; ++i) {
+    a.cs2[i] = out_res->code_stride[i];
+    a.ss2[i] = out_res->scale_stride[i];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_quantize_batch(&a, 1, s), s, "quantize_dual");
+}
+
 mxattn_status_t mxattn_quantize_batch(const mxattn_quantize_job_t* jobs, int32_t n_jobs, mxattn_stream_t stream) {
   mxattn_status_t st;
   if (injected("quantize_batch", &st)) return st;
@@ -292,7 +315,7 @@ size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int
   return bytes;
 }
 
-mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mxattn_mx_t* kc,
+mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16, const mxattn_mx_t* kc,
                               const mxattn_mx_t* vc, const int32_t* ctx_len, const mxattn_hybrid_t* hy,
                               float softmax_scale, int32_t split_len, void* workspace, size_t workspace_bytes,
                               float* out, float* lse, mxattn_stream_t stream) {
@@ -303,6 +326,11 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
   if ((st = check_mx(vc, "decode.v_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if (ctx_len == nullptr || out == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode: null ctx_len/out");
   if (q->seq != 1) return fail(MXATTN_ERR_UNSUPPORTED, "decode: one query token per sequence");
+  if (q_res != nullptr) {
+    if ((st = check_mx(q_res, "decode.q_res", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+    if (q_res->batch != q->batch || q_res->heads != q->heads || q_res->seq != q->seq || q_res->dim != q->dim)
+      return fail(MXATTN_ERR_INVALID_ARG, "decode: q_res shape differs from q");
+  }
   if (q->dim != kc->dim || kc->dim != vc->dim) return fail(MXATTN_ERR_INVALID_ARG, "decode: head_dim mismatch");
   if (q->batch != kc->batch || kc->batch != vc->batch) return fail(MXATTN_ERR_INVALID_ARG, "decode: batch mismatch");
   if (kc->heads != vc->heads || kc->seq != vc->seq) return fail(MXATTN_ERR_INVALID_ARG, "decode: K/V cache shape mismatch");
@@ -338,6 +366,8 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mx
   if (!aligned16(workspace)) return fail(MXATTN_ERR_INVALID_ARG, "decode: workspace not 16-byte aligned");
   DecodeArgs a{};
   a.q = view_of(q);
+  a.dual = q_res != nullptr;
+  if (a.dual) a.q2 = view_of(q_res);
   a.k = view_of(kc);
   a.v = view_of(vc);
   a.ctx_len = ctx_len;

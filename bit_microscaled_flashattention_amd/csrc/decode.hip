@@ -232,7 +232,9 @@ constexpr int kMaxSplitWords = 8192 / 32;
 // final combine.  Every load is unconditional (range-checked by the buffer
 // resource), which keeps the wait counts exact: the scan of one chunk waits
 // only for that chunk's bytes.
-template <int D>
+// DUAL: the query is a dual-residual pair (a.q, a.q2); each logit MFMA is
+// followed by one against the residual query, accumulating into it.
+template <int D, bool DUAL>
 __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, uint32_t* selbits, int split,
                                           int hk, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -246,14 +248,20 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
   const int t_end = max(t_begin, min(t_begin + a.split_len, end4));
 
   // Query operand: column j (query head hk*G + j), channels [32g, 32g+32).
-  v4i qop = {0, 0, 0, 0};
-  int qsc = 0;
+  v4i qop = {0, 0, 0, 0}, qop2 = {0, 0, 0, 0};
+  int qsc = 0, qsc2 = 0;
   if (j < G && g < D / 32) {
     const int hq = hk * G + j;
     const uint8_t* qc = a.q.codes + b * a.q.cs[0] + hq * a.q.cs[1];
     const uint8_t* qs = a.q.scales + b * a.q.ss[0] + hq * a.q.ss[1];
     qop = *reinterpret_cast<const v4i*>(qc + g * 16);
     qsc = qs[g];
+    if constexpr (DUAL) {
+      const uint8_t* qc2 = a.q2.codes + b * a.q2.cs[0] + hq * a.q2.cs[1];
+      const uint8_t* qs2 = a.q2.scales + b * a.q2.ss[0] + hq * a.q2.ss[1];
+      qop2 = *reinterpret_cast<const v4i*>(qc2 + g * 16);
+      qsc2 = qs2[g];
+    }
   }
   const int64_t kcs = a.k.cs[2], kss = a.k.ss[2], vcs = a.v.cs[2], vss = a.v.ss[2];
   const __amdgpu_buffer_rsrc_t rkc = make_rsrc(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], uint32_t(t_end * kcs));
@@ -309,8 +317,12 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
 
   auto process = [&](const ChunkRegs& r, int t0) {
     stage_v<D>(r, vr, lane);
-    const v4f s0 = mfma16_fp4(r.k[0], qop, v4f{0, 0, 0, 0}, r.ks[0], qsc);
-    const v4f s1 = mfma16_fp4(r.k[1], qop, v4f{0, 0, 0, 0}, r.ks[1], qsc);
+    v4f s0 = mfma16_fp4(r.k[0], qop, v4f{0, 0, 0, 0}, r.ks[0], qsc);
+    v4f s1 = mfma16_fp4(r.k[1], qop, v4f{0, 0, 0, 0}, r.ks[1], qsc);
+    if constexpr (DUAL) {
+      s0 = mfma16_fp4(r.k[0], qop2, s0, r.ks[0], qsc2);
+      s1 = mfma16_fp4(r.k[1], qop2, s1, r.ks[1], qsc2);
+    }
     float sv[8];
     const uint32_t mw = a.hybrid ? selbits[(t0 - t_begin) >> 5] : 0u;   // chunks are 32-aligned
 #pragma unroll
@@ -474,12 +486,12 @@ __device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, 
 
 // One launch for the whole scan: blockIdx.x < n_split are the 4-bit splits,
 // the rest the bf16 hybrid parts, so the two kinds share the machine.
-template <int D>
+template <int D, bool DUAL>
 __global__ __launch_bounds__(kDecThreads, 3) void decode_scan_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
   __shared__ uint32_t selbits[kMaxSplitWords];
   if (static_cast<int>(blockIdx.x) < a.n_split)
-    fp4_split<D>(a, vstage, selbits, blockIdx.x, blockIdx.y, blockIdx.z);
+    fp4_split<D, DUAL>(a, vstage, selbits, blockIdx.x, blockIdx.y, blockIdx.z);
   else
     bf16_part<D>(a, vstage, blockIdx.x - a.n_split, blockIdx.y, blockIdx.z);
 }
@@ -536,10 +548,16 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {
   const dim3 grid(a.n_split + (a.hybrid ? a.n_bf16 : 0), a.Hkv, a.B);
   if (D == 128) {
-    hipLaunchKernelGGL(decode_scan_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
+    if (a.dual)
+      hipLaunchKernelGGL((decode_scan_kernel<128, true>), grid, dim3(kDecThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_scan_kernel<128, false>), grid, dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.Hq, a.B), dim3(128), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_scan_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
+    if (a.dual)
+      hipLaunchKernelGGL((decode_scan_kernel<64, true>), grid, dim3(kDecThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_scan_kernel<64, false>), grid, dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.Hq, a.B), dim3(64), 0, stream, a);
   }
   return hipGetLastError();

@@ -20,6 +20,12 @@ struct QuantArgs {
   uint8_t* scales;
   int64_t cs[3];
   int64_t ss[3];
+  // Dual residual (head-dim blocks only): codes2/scales2 receive the MXFP4
+  // of x - dequant(codes, scales); null when unused.
+  uint8_t* codes2;
+  uint8_t* scales2;
+  int64_t cs2[3];
+  int64_t ss2[3];
 };
 
 // bf16 hybrid rows per decode workgroup (one partial slot each), and the
@@ -75,6 +81,8 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   MxView q, k, v;
+  MxView q2;            // residual query of a dual-residual split (when dual)
+  int dual;
   const int32_t* ctx_len;
   int B, Hq, Hkv, Tcap;
   float c;

@@ -54,6 +54,17 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, int sb) {
   return c | sign;
 }
 
+// Exact value of a 4-bit code under scale byte sb: the E2M1 magnitude built
+// as fp32 bits (0, 0.5, or 2^(e-1) (1 + m/2) for exponent field e >= 1)
+// times 2^(sb-127) through ldexp, which is exact here because subnormal
+// results are kept.
+__device__ __forceinline__ float e2m1_value(uint32_t code, int sb) {
+  const uint32_t c3 = code & 7u;
+  const uint32_t bits = c3 == 0 ? 0u : (c3 == 1 ? (126u << 23) : (((126u + (c3 >> 1)) << 23) | ((c3 & 1u) << 22)));
+  const float mag = __builtin_ldexpf(__uint_as_float(bits), sb - 127);
+  return (code & 8u) ? -mag : mag;
+}
+
 // Scaled FP4 x FP4 MFMAs (E2M1 both sides, one E8M0 scale per lane held in
 // byte 0 of the scale operand).
 __device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f c, int sa, int sb) {

@@ -134,10 +134,32 @@ __device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h
     amax = quad_max(amax);
     const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
     const uint32_t packed = encode8(y[r], sb);
+    uint32_t packed2 = 0;
+    int sb2 = 0;
+    if (a.codes2 != nullptr) {
+      // Dual residual: x - dequant(code), exact in fp32 (the dequantised value
+      // is 0 or within a factor of two of x), encoded the same way.
+      float res[8];
+      uint32_t amax2 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        res[i] = y[r][i] - e2m1_value((packed >> (4 * i)) & 0xFu, sb);
+        const uint32_t m2 = __float_as_uint(res[i]) & 0x7FFFFFFFu;
+        amax2 = m2 > amax2 ? m2 : amax2;
+      }
+      amax2 = quad_max(amax2);
+      sb2 = e8m0_byte(amax2, a.uos, a.qmax_quarter);
+      packed2 = encode8(res, sb2);
+    }
     if (blk >= total) continue;
     uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + s * a.cs[2];
     *reinterpret_cast<uint32_t*>(crow + d0 / 2) = packed;
     if (part == 0) a.scales[b * a.ss[0] + h * a.ss[1] + s * a.ss[2] + db] = static_cast<uint8_t>(sb);
+    if (a.codes2 != nullptr) {
+      uint8_t* crow2 = a.codes2 + b * a.cs2[0] + h * a.cs2[1] + s * a.cs2[2];
+      *reinterpret_cast<uint32_t*>(crow2 + d0 / 2) = packed2;
+      if (part == 0) a.scales2[b * a.ss2[0] + h * a.ss2[1] + s * a.ss2[2] + db] = static_cast<uint8_t>(sb2);
+    }
   }
 }
 

@@ -106,6 +106,22 @@ mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int
                                 const mxattn_mx_t* out, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * mxattn_quantize_dual -- dual-residual MXFP4 (BitDecoding-FP4, "Dual-Residual
+ * Query Quantization": the query split into two FP4 tensors).  `out`
+ * receives exactly what mxattn_quantize writes for the same arguments;
+ * `out_res` receives the MXFP4 encoding, same rule and blocks, of the
+ * residual x' - dequant(out), where x' is x after the optional channel
+ * multiply.  The residual is formed in fp32 and is exact (the dequantised
+ * value is 0 or within a factor of two of x').  Pass both to mxattn_decode
+ * (q and q_res): the logits then use dequant(out) + dequant(out_res).
+ * Both descriptors must use the HD layout and the same shape
+ * (MXATTN_ERR_UNSUPPORTED for KEY, MXATTN_ERR_INVALID_ARG for a shape
+ * mismatch); the other arguments and checks are those of mxattn_quantize. */
+mxattn_status_t mxattn_quantize_dual(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
+                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                     const mxattn_mx_t* out, const mxattn_mx_t* out_res, mxattn_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * mxattn_quantize_batch -- the same encoding as mxattn_quantize for up to
  * MXATTN_MAX_QUANTIZE_JOBS tensors in one launch (for instance the Q, K and
  * V of one attention call, which are too small to fill the device one at a
@@ -181,6 +197,10 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
  * dequantisation fused into the scan, optionally with a bf16 hybrid token set
  * under the same softmax (HyQuant, method paragraphs).
  *   q        HD layout [B][Hq][1][D] (MXFP4 query).
+ *   q_res    nullable; HD layout, same shape: the residual part of a
+ *            dual-residual query (mxattn_quantize_dual).  The 4-bit logits
+ *            then use dequant(q) + dequant(q_res) (one more QK^T MFMA per
+ *            chunk); the bf16 hybrid tokens keep using q_bf16.
  *   q_bf16   bf16 [B][Hq][D] contiguous; read only when hybrid != NULL.
  *   k_cache, v_cache  HD layout [B][Hkv][Tcap][D].
  *   ctx_len  device int32 [B]; token t of sequence b is attended iff
@@ -217,7 +237,8 @@ typedef struct {
 size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int64_t dim,
                                      int64_t tcap, int32_t split_len, int32_t hybrid_rows);
 
-mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const void* q_bf16, const mxattn_mx_t* k_cache,
+mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,
+                              const mxattn_mx_t* k_cache,
                               const mxattn_mx_t* v_cache, const int32_t* ctx_len,
                               const mxattn_hybrid_t* hybrid, float softmax_scale,
                               int32_t split_len, void* workspace, size_t workspace_bytes,

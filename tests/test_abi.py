@@ -158,24 +158,47 @@ def test_decode_workspace_and_rejects():
     ctx = ctypes.c_void_p(64)
     out = ctypes.c_void_p(4096)
     # workspace too small
-    st = lib.mxattn_decode(ctypes.byref(q), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 2048,
+    st = lib.mxattn_decode(ctypes.byref(q), None, None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 2048,
                            ctypes.c_void_p(4096), 16, out, None, None)
     assert st == mxa.ERR_WORKSPACE
     # split_len not a multiple of 64
-    st = lib.mxattn_decode(ctypes.byref(q), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 100,
+    st = lib.mxattn_decode(ctypes.byref(q), None, None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 100,
                            ctypes.c_void_p(4096), 1 << 30, out, None, None)
     assert st == mxa.ERR_UNSUPPORTED
     # group of 3 query heads per KV head
     q3 = _mx(s=1, h=24)
-    st = lib.mxattn_decode(ctypes.byref(q3), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 2048,
+    st = lib.mxattn_decode(ctypes.byref(q3), None, None, ctypes.byref(kc), ctypes.byref(vc), ctx, None, 0.0, 2048,
                            ctypes.c_void_p(4096), 1 << 30, out, None, None)
     assert st == mxa.ERR_UNSUPPORTED
     # hybrid without a bf16 query
     hy = mxa._Hybrid()
     hy.max_sel, hy.window = 16, 8
-    st = lib.mxattn_decode(ctypes.byref(q), None, ctypes.byref(kc), ctypes.byref(vc), ctx, ctypes.byref(hy),
+    st = lib.mxattn_decode(ctypes.byref(q), None, None, ctypes.byref(kc), ctypes.byref(vc), ctx, ctypes.byref(hy),
                            0.0, 2048, ctypes.c_void_p(4096), 1 << 30, out, None, None)
     assert st == mxa.ERR_INVALID_ARG
+    # residual query of another shape
+    qr = _mx(s=1, h=16)
+    st = lib.mxattn_decode(ctypes.byref(q), ctypes.byref(qr), None, ctypes.byref(kc), ctypes.byref(vc), ctx, None,
+                           0.0, 2048, ctypes.c_void_p(4096), 1 << 30, out, None, None)
+    assert st == mxa.ERR_INVALID_ARG
+    assert b"q_res" in lib.mxattn_last_error()
+
+
+def test_quantize_dual_rejects_without_launch():
+    lib = mxa.library()
+    strides = (ctypes.c_int64 * 3)(0, 0, 128)
+    out, res = _mx(), _mx()
+    x = ctypes.c_void_p(64)
+    # KEY layout
+    kout = _mx(layout=1)
+    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, ctypes.byref(kout), ctypes.byref(res), None) == \
+        mxa.ERR_UNSUPPORTED
+    # shapes differ
+    res2 = _mx(s=65)
+    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, ctypes.byref(out), ctypes.byref(res2), None) == \
+        mxa.ERR_INVALID_ARG
+    # null residual descriptor
+    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, ctypes.byref(out), None, None) == mxa.ERR_INVALID_ARG
 
 
 def test_select_rejects():

@@ -99,6 +99,42 @@ def test_decode_split_and_tiny_context():
     np.testing.assert_allclose(outs[0][0, 0].cpu().numpy(), vd, atol=1e-6)
 
 
+def test_decode_dual_residual_query():
+    """A dual-residual query (q1, q2) scores every 4-bit token with
+    dequant(q1) + dequant(q2): parity with the oracle on that query, and the
+    outputs move towards attention with the unquantised query."""
+    g = torch.Generator(device=DEV).manual_seed(36)
+    b, hq, hkv, tcap, d = 2, 8, 2, 1500, 128
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    q[:, :, 3] *= 12
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([1500, 999], dtype=torch.int32, device=DEV)
+    kc, vc = _cache(k, v)
+    q1, q2 = mxa.quantize_dual(q[:, :, None, :])
+    print("decode dual-residual query", flush=True)
+    out_d, lse_d = mxa.decode(q1, kc, vc, ctx, split_len=512, return_lse=True, q_res=q2)
+    out_s = mxa.decode(q1, kc, vc, ctx, split_len=512)
+    torch.cuda.synchronize()
+    c1, s1, c2, s2 = mx.quantize_dual(host_f64(q[:, :, None, :]), axis=3)
+    q_hat = (oracle_dequant(c1, s1, "hd") + oracle_dequant(c2, s2, "hd"))[:, :, 0]
+    q_ex = host_f64(q)
+    ref, ref_exact = {}, {}
+    for bb in range(b):
+        for h in range(hq):
+            kv = h // (hq // hkv)
+            kd = oracle_dequant(*oracle_quantize(host_f64(k[bb:bb + 1, kv:kv + 1]), "hd"), "hd")[0, 0]
+            vd = oracle_dequant(*oracle_quantize(host_f64(v[bb:bb + 1, kv:kv + 1]), "hd"), "hd")[0, 0]
+            ref[(bb, h)] = attention.decode_head(q_hat[bb, h], kd, vd, int(ctx[bb]))
+            ref_exact[(bb, h)] = attention.decode_head(q_ex[bb, h], kd, vd, int(ctx[bb]))[0]
+    _compare(out_d, lse_d, ref, "dual-residual decode")
+    od, os_ = out_d.cpu().numpy(), out_s.cpu().numpy()
+    err_d = np.mean([np.abs(od[bb, h] - ref_exact[(bb, h)]).mean() for (bb, h) in ref_exact])
+    err_s = np.mean([np.abs(os_[bb, h] - ref_exact[(bb, h)]).mean() for (bb, h) in ref_exact])
+    print(f"  mean |out - out(exact q)|: single {err_s:.3e}, dual {err_d:.3e}", flush=True)
+    assert err_d < err_s / 2
+
+
 def _hybrid_inputs(q, k, v, ctx, window, n_sel, max_sel, seed):
     """Seeded selected sets (ascending, below ctx-window) and the gathered
     bf16 rows the decode reads."""

@@ -109,6 +109,33 @@ def test_workload_shapes_q_k_v():
         assert_codes_equal(got, oc, os_, f"4K GQA prefill {name}")
 
 
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_quantize_dual_bit_exact(rule):
+    """Both halves of the dual-residual query, codes and scale bytes, bit for
+    bit: ordinary bf16 rows with channel factors, and fp32 blocks whose
+    maxima sit in and around the subnormal range."""
+    g = torch.Generator().manual_seed(41)
+    x = (torch.randn((2, 4, 37, 128), generator=g) * 3).to(torch.bfloat16)
+    x[:, :, :, 7] *= 25
+    cs = torch.exp(torch.randn((4, 128), generator=g)).to(torch.float32)
+    tiny = _tiny_magnitude_blocks()[:, :, :200]
+    r = mx.RULE_OCP if rule == "ocp" else mx.RULE_UOS
+    for xin, csin, what in ((x, cs, "bf16 with channel factors"), (tiny, None, "fp32 tiny blocks")):
+        print(f"quantize_dual {rule} {what}", flush=True)
+        q1, q2 = mxa.quantize_dual(xin.to(DEV), chan_scale=csin.to(DEV) if csin is not None else None, rule=rule)
+        torch.cuda.synchronize()
+        x64 = host_f64(xin)
+        if csin is not None:
+            x64 = smooth.apply(x64.astype(np.float32), csin.numpy()).astype(np.float64)
+        c1, s1, c2, s2 = mx.quantize_dual(x64, axis=3, rule=r)
+        assert_codes_equal(q1, c1, s1, f"dual first half, {what}")
+        assert_codes_equal(q2, c2, s2, f"dual residual half, {what}")
+        # The first half is what quantize() writes.
+        q0 = mxa.quantize(xin.to(DEV), chan_scale=csin.to(DEV) if csin is not None else None, rule=rule)
+        torch.cuda.synchronize()
+        assert torch.equal(q0.codes, q1.codes) and torch.equal(q0.scales, q1.scales)
+
+
 def _batch_case(seed=21):
     """Four jobs that differ in dtype, layout, rule, head_dim, sequence length
     (ragged, and a single token) and input strides (a sliced, non-contiguous
