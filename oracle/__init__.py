@@ -6,8 +6,9 @@ CPU-baseline leg use it.  It shares no code, table or helper with the HIP
 library; the two meet only through the seeded input generators in ``synth``.
 
 Everything here is numpy.  Integer work (codes, scale bytes, indices) is exact;
-attention arithmetic runs in float64.  The one float32 step is the Smooth-QK
-channel multiply, which the method defines on float32 activations.
+attention arithmetic runs in float64.  The float32 steps are the Smooth-QK
+channel multiply, which the method defines on float32 activations, and the
+Hadamard rotation that feeds the quantiser.
 
 Modules
   mx         -- E2M1 element / E8M0 scale codec (OCP rule and the UOS bound)
@@ -15,8 +16,9 @@ Modules
   attention  -- tiled online-softmax prefill with pre-normalisation P
                 quantisation, and the (hybrid) decode softmax
   select     -- accumulated column mass and top-rho vertical-line selection
+  rotate     -- Hadamard rotation of query/key rows before quantisation
 
 Parity status per function is stated in each module's header.
 """
 
-from . import mx, smooth, attention, select  # noqa: F401
+from . import mx, smooth, attention, select, rotate  # noqa: F401
