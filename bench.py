@@ -132,12 +132,27 @@ def prefill_leg(args):
         mxa.quantize_batch(qkv_jobs)
         attn()
 
+    # The same step with Q and K rotated by the Walsh-Hadamard transform inside
+    # the quantiser; the attention kernel is unchanged.
+    rot_jobs = [dict(j, hadamard=True) if j.get("layout", "hd") == "hd" else j for j in qkv_jobs]
+
+    def step_rot():
+        mxa.quantize_batch(rot_jobs)
+        attn()
+
     wall, kern = timed(step, args.steps, args.warmup, attn)
+    _, quant = timed(lambda: None, args.steps, 0, lambda: mxa.quantize_batch(qkv_jobs))
+    wall_r, quant_r = timed(step_rot, args.steps, args.warmup, lambda: mxa.quantize_batch(rot_jobs))
     pairs = B * HQ * S * (S + 1) // 2
     flops = 4 * D * pairs
     res = {
         "flops": flops, "step_s": wall, "kernel_s": kern,
         "step_tflops": flops / wall / 1e12, "kernel_tflops": flops / kern / 1e12,
+        "quantize_s": quant,
+        "hadamard_qk": {"ms_per_step": round(wall_r * 1e3, 4), "step_tflops": round(flops / wall_r / 1e12, 2),
+                        "quantize_ms": round(quant_r * 1e3, 4), "plain_quantize_ms": round(quant * 1e3, 4),
+                        "note": "Q and K rows rotated by the normalised Walsh-Hadamard transform before MXFP4 "
+                                "(in the quantiser launch); same attention kernel"},
     }
     return res, d, (qs, ks)
 
@@ -381,6 +396,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(pre["kernel_tflops"] / PEAK_FP4_TFLOPS, 4),
                      "kernel_ms": round(pre["kernel_s"] * 1e3, 4),
                      "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,true,true>")},
+        "hadamard_qk": pre["hadamard_qk"],
     }
     del d
     torch.cuda.empty_cache()

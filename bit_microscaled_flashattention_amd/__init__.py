@@ -49,7 +49,7 @@ class _Mx(ctypes.Structure):
 
 class _QuantJob(ctypes.Structure):
     _fields_ = [
-        ("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("x_stride", ctypes.c_int64 * 3), ("chan_scale", ctypes.c_void_p),
         ("rule", ctypes.c_int32), ("qmax", ctypes.c_float), ("out", ctypes.POINTER(_Mx)),
     ]
@@ -82,12 +82,12 @@ def _load():
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     P = ctypes.POINTER
     sig = {
-        "mxattn_quantize": [vp, i32, P(i64), vp, i32, f32, P(_Mx), vp],
+        "mxattn_quantize": [vp, i32, P(i64), vp, i32, f32, i32, P(_Mx), vp],
         "mxattn_quantize_batch": [P(_QuantJob), i32, vp],
         "mxattn_smooth_calibrate": [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp],
         "mxattn_prefill": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), vp, i32, vp, vp],
         "mxattn_decode": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
-        "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, P(_Mx), P(_Mx), vp],
+        "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, i32, P(_Mx), P(_Mx), vp],
         "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
     }
     for name, args in sig.items():
@@ -184,8 +184,12 @@ def empty_mx(shape, layout="hd", device="cuda"):
     return MX(codes, scales, tuple(shape), layout)
 
 
-def quantize(x, layout="hd", chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None):
-    """MXFP4-encode x [B,H,S,D] (bf16/fp16/fp32, last dim contiguous)."""
+QUANT_HADAMARD = 1
+
+
+def quantize(x, layout="hd", chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None, hadamard=False):
+    """MXFP4-encode x [B,H,S,D] (bf16/fp16/fp32, last dim contiguous).
+    hadamard=True rotates each head-dim row first (rotate Q and K alike)."""
     assert x.dim() == 4 and x.stride(3) == 1, "x must be [B,H,S,D] with contiguous D"
     if out is None:
         out = empty_mx(tuple(x.shape), layout, x.device)
@@ -195,11 +199,11 @@ def quantize(x, layout="hd", chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=Non
         cs = chan_scale.to(torch.float32).contiguous()
     d = out.desc()
     _check(_lib.mxattn_quantize(_ptr(x), _DT[x.dtype], strides, _ptr(cs), _RULES[rule],
-                                float(qmax), ctypes.byref(d), _stream(x)))
+                                float(qmax), QUANT_HADAMARD if hadamard else 0, ctypes.byref(d), _stream(x)))
     return out
 
 
-def quantize_dual(x, chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None, out_res=None):
+def quantize_dual(x, chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None, out_res=None, hadamard=False):
     """Dual-residual MXFP4 of x [B,H,S,D] (HD blocks): returns (q1, q2) with
     q1 = quantize(x) and q2 the MXFP4 of x - dequant(q1)."""
     assert x.dim() == 4 and x.stride(3) == 1, "x must be [B,H,S,D] with contiguous D"
@@ -211,7 +215,8 @@ def quantize_dual(x, chan_scale=None, rule="ocp", qmax=UOS_QMAX, out=None, out_r
     cs = chan_scale.to(torch.float32).contiguous() if chan_scale is not None else None
     d1, d2 = out.desc(), out_res.desc()
     _check(_lib.mxattn_quantize_dual(_ptr(x), _DT[x.dtype], strides, _ptr(cs), _RULES[rule], float(qmax),
-                                     ctypes.byref(d1), ctypes.byref(d2), _stream(x)))
+                                     QUANT_HADAMARD if hadamard else 0, ctypes.byref(d1), ctypes.byref(d2),
+                                     _stream(x)))
     return out, out_res
 
 
@@ -240,6 +245,7 @@ def quantize_batch(jobs):
         arr[i].chan_scale = _ptr(cs)
         arr[i].rule = _RULES[j.get("rule", "ocp")]
         arr[i].qmax = float(j.get("qmax", UOS_QMAX))
+        arr[i].flags = QUANT_HADAMARD if j.get("hadamard", False) else 0
         arr[i].out = ctypes.pointer(d)
         outs.append(out)
     _check(_lib.mxattn_quantize_batch(arr, len(jobs), _stream(jobs[0]["x"])))

@@ -135,7 +135,7 @@ const char* mxattn_status_string(mxattn_status_t s) {
 // Validates one quantisation request and fills its kernel arguments.
 static mxattn_status_t quantize_args(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
                                      const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
-                                     const mxattn_mx_t* out, const char* name, QuantArgs* a) {
+                                     int32_t flags, const mxattn_mx_t* out, const char* name, QuantArgs* a) {
   mxattn_status_t st;
   if (x == nullptr || x_stride == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "%s: null input", name);
   if (x_dtype != MXATTN_F32 && x_dtype != MXATTN_F16 && x_dtype != MXATTN_BF16)
@@ -144,6 +144,9 @@ static mxattn_status_t quantize_args(const void* x, mxattn_dtype_t x_dtype, cons
   if (rule == MXATTN_SCALE_UOS && !valid_qmax(qmax))
     return fail(MXATTN_ERR_UNSUPPORTED, "%s: UOS qmax must lie in (4, 8)", name);
   if ((st = check_mx(out, name, -1)) != MXATTN_OK) return st;
+  if ((flags & ~MXATTN_QUANT_HADAMARD) != 0) return fail(MXATTN_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, flags);
+  if ((flags & MXATTN_QUANT_HADAMARD) && out->layout != MXATTN_LAYOUT_HD)
+    return fail(MXATTN_ERR_UNSUPPORTED, "%s: the Hadamard rotation needs the HD layout", name);
   for (int i = 0; i < 3; ++i)
     if (x_stride[i] < 0) return fail(MXATTN_ERR_INVALID_ARG, "%s: negative input stride", name);
   // Rows are read 8 elements (16 or 32 bytes) at a time.
@@ -165,6 +168,8 @@ static mxattn_status_t quantize_args(const void* x, mxattn_dtype_t x_dtype, cons
   a->uos = rule == MXATTN_SCALE_UOS;
   a->qmax_quarter = qmax * 0.25f;
   a->key_layout = out->layout == MXATTN_LAYOUT_KEY;
+  a->hadamard = (flags & MXATTN_QUANT_HADAMARD) != 0;
+  a->rot_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(out->dim)));
   a->B = out->batch;
   a->H = out->heads;
   a->S = out->seq;
@@ -175,23 +180,25 @@ static mxattn_status_t quantize_args(const void* x, mxattn_dtype_t x_dtype, cons
 }
 
 mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
-                                const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                const float* chan_scale, mxattn_scale_rule_t rule, float qmax, int32_t flags,
                                 const mxattn_mx_t* out, mxattn_stream_t stream) {
   mxattn_status_t st;
   if (injected("quantize", &st)) return st;
   QuantArgs a;
-  if ((st = quantize_args(x, x_dtype, x_stride, chan_scale, rule, qmax, out, "quantize", &a)) != MXATTN_OK) return st;
+  if ((st = quantize_args(x, x_dtype, x_stride, chan_scale, rule, qmax, flags, out, "quantize", &a)) != MXATTN_OK)
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return after_launch(launch_quantize_batch(&a, 1, s), s, "quantize");
 }
 
 mxattn_status_t mxattn_quantize_dual(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
-                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax, int32_t flags,
                                      const mxattn_mx_t* out, const mxattn_mx_t* out_res, mxattn_stream_t stream) {
   mxattn_status_t st;
   if (injected("quantize_dual", &st)) return st;
   QuantArgs a;
-  if ((st = quantize_args(x, x_dtype, x_stride, chan_scale, rule, qmax, out, "quantize_dual", &a)) != MXATTN_OK)
+  if ((st = quantize_args(x, x_dtype, x_stride, chan_scale, rule, qmax, flags, out, "quantize_dual", &a)) !=
+      MXATTN_OK)
     return st;
   if (out->layout != MXATTN_LAYOUT_HD) return fail(MXATTN_ERR_UNSUPPORTED, "quantize_dual: out must use the HD layout");
   if ((st = check_mx(out_res, "quantize_dual.out_res", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
@@ -219,7 +226,8 @@ mxattn_status_t mxattn_quantize_batch(const mxattn_quantize_job_t* jobs, int32_t
     char name[40];
     snprintf(name, sizeof(name), "quantize_batch.job[%d]", i);
     const mxattn_quantize_job_t& j = jobs[i];
-    if ((st = quantize_args(j.x, j.x_dtype, j.x_stride, j.chan_scale, j.rule, j.qmax, j.out, name, &a[i])) != MXATTN_OK)
+    if ((st = quantize_args(j.x, j.x_dtype, j.x_stride, j.chan_scale, j.rule, j.qmax, j.flags, j.out, name, &a[i])) !=
+        MXATTN_OK)
       return st;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

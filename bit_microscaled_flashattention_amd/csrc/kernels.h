@@ -15,6 +15,8 @@ struct QuantArgs {
   int uos;
   float qmax_quarter;
   int key_layout;
+  int hadamard;         // rotate each head-dim row before quantising
+  float rot_scale;      // float32(1 / sqrt(D))
   int64_t B, H, S, D;
   uint8_t* codes;
   uint8_t* scales;

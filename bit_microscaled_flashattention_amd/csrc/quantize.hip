@@ -120,6 +120,37 @@ __device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h
         y[r][4 + k] = __fmul_rn(y[r][4 + k], c1[k]);
       }
   }
+  if (a.hadamard) {
+    // Normalised Walsh-Hadamard transform of each row (BitDecoding-FP4,
+    // key outliers): element d = 8 (lane % lanes_per_row) + i.  Butterflies
+    // (a, b) -> (a + b, a - b) on pairs (d, d + h), h = 1, 2, 4 inside the
+    // lane, then h = 8 ... D/2 between lane and lane ^ (h / 8); every sum is
+    // rounded to fp32 in that stage order, then one multiply by
+    // fp32(1/sqrt(D)).
+    const int row_lanes = static_cast<int>(a.D) / 8;   // 16 or 8
+#pragma unroll
+    for (int r = 0; r < kHdRows; ++r) {
+#pragma unroll
+      for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if ((i & hs) == 0) {
+            const float u = y[r][i], w = y[r][i + hs];
+            y[r][i] = u + w;
+            y[r][i + hs] = u - w;
+          }
+      for (int m = 1; m < row_lanes; m <<= 1) {
+        const bool high = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float other = __shfl_xor(y[r][i], m);
+          y[r][i] = high ? other - y[r][i] : y[r][i] + other;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[r][i] = __fmul_rn(y[r][i], a.rot_scale);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kHdRows; ++r) {
     const int blk = (wave * kHdRows + r) * 16 + (lane >> 2);

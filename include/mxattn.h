@@ -95,14 +95,24 @@ typedef struct {
  *              multiplied by chan_scale[h][d] in IEEE fp32 (round to nearest
  *              even); the block maximum and codes are taken from that product.
  *   rule,qmax  the E8M0 rule (qmax is read for UOS only).
+ *   flags      0, or MXATTN_QUANT_HADAMARD: after the channel multiply each
+ *              head-dim row is rotated by the normalised Walsh-Hadamard
+ *              transform (BitDecoding-FP4, key outliers: Hadamard rotation),
+ *              computed in fp32 as butterflies (a, b) -> (a + b, a - b) on
+ *              element pairs (i, i + h), i & h = 0, for h = 1, 2, ..., D/2 in
+ *              that order, then one multiply by fp32(1/sqrt(D)).  Rotate Q
+ *              and K alike (dot products are unchanged), never V.  HD layout
+ *              only (MXATTN_ERR_UNSUPPORTED otherwise); other bits are
+ *              MXATTN_ERR_INVALID_ARG.
  *   out        destination; out->{batch,heads,seq,dim} must equal the input
  *              shape, out->layout selects the block axis.
  * Codes are round-to-nearest-even onto {0,.5,1,1.5,2,3,4,6} of x/2^e, ties to
  * the even code, saturating at 6, sign kept (a negative value that rounds to
  * zero is code 8).  Supported: D in {64, 128}; any S >= 1 (HD) or S >= 1 with
  * padding (KEY).  Cost: one pass over x (HBM-bound). */
+#define MXATTN_QUANT_HADAMARD 1
 mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
-                                const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                const float* chan_scale, mxattn_scale_rule_t rule, float qmax, int32_t flags,
                                 const mxattn_mx_t* out, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -118,7 +128,7 @@ mxattn_status_t mxattn_quantize(const void* x, mxattn_dtype_t x_dtype, const int
  * (MXATTN_ERR_UNSUPPORTED for KEY, MXATTN_ERR_INVALID_ARG for a shape
  * mismatch); the other arguments and checks are those of mxattn_quantize. */
 mxattn_status_t mxattn_quantize_dual(const void* x, mxattn_dtype_t x_dtype, const int64_t x_stride[3],
-                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax,
+                                     const float* chan_scale, mxattn_scale_rule_t rule, float qmax, int32_t flags,
                                      const mxattn_mx_t* out, const mxattn_mx_t* out_res, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -137,7 +147,7 @@ mxattn_status_t mxattn_quantize_dual(const void* x, mxattn_dtype_t x_dtype, cons
 typedef struct {
   const void* x;
   mxattn_dtype_t x_dtype;
-  int32_t reserved;
+  int32_t flags;   /* as mxattn_quantize */
   int64_t x_stride[3];
   const float* chan_scale;
   mxattn_scale_rule_t rule;

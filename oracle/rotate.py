@@ -22,7 +22,7 @@ Readings taken where the source is silent:
     float32(1 / sqrt(D)).  Both sides take every rounding decision the same
     way.
 
-Parity: pinned by tests/test_oracle_codec.py -- the float64 transform equals
+Parity: pinned by tests/test_oracle_rotate.py -- the float64 transform equals
 the Sylvester matrix product (scipy.linalg.hadamard), the float32 transform
 stays within the rounding bound of that product, applying it twice returns
 the row, and dot products are preserved.

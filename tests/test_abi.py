@@ -106,10 +106,22 @@ def test_quantize_rejects_without_launch():
     lib = mxa.library()
     out = _mx()
     strides = (ctypes.c_int64 * 3)(0, 0, 128)
-    assert lib.mxattn_quantize(None, 2, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
-    assert lib.mxattn_quantize(ctypes.c_void_p(64), 7, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
-    assert lib.mxattn_quantize(ctypes.c_void_p(64), 2, strides, None, 1, 8.5, ctypes.byref(out), None) == mxa.ERR_UNSUPPORTED
-    assert lib.mxattn_quantize(ctypes.c_void_p(65), 2, strides, None, 0, 7.25, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize(None, 2, strides, None, 0, 7.25, 0, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize(ctypes.c_void_p(64), 7, strides, None, 0, 7.25, 0, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize(ctypes.c_void_p(64), 2, strides, None, 1, 8.5, 0, ctypes.byref(out), None) == mxa.ERR_UNSUPPORTED
+    assert lib.mxattn_quantize(ctypes.c_void_p(65), 2, strides, None, 0, 7.25, 0, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+
+
+def test_quantize_flags_rejects_without_launch():
+    lib = mxa.library()
+    strides = (ctypes.c_int64 * 3)(0, 0, 128)
+    out, kout = _mx(), _mx(layout=1)
+    x = ctypes.c_void_p(64)
+    assert lib.mxattn_quantize(x, 2, strides, None, 0, 7.25, 4, ctypes.byref(out), None) == mxa.ERR_INVALID_ARG
+    assert b"flags" in lib.mxattn_last_error()
+    assert lib.mxattn_quantize(x, 2, strides, None, 0, 7.25, mxa.QUANT_HADAMARD, ctypes.byref(kout), None) == \
+        mxa.ERR_UNSUPPORTED
+    assert b"Hadamard" in lib.mxattn_last_error()
 
 
 def test_quantize_batch_rejects_without_launch():
@@ -191,14 +203,14 @@ def test_quantize_dual_rejects_without_launch():
     x = ctypes.c_void_p(64)
     # KEY layout
     kout = _mx(layout=1)
-    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, ctypes.byref(kout), ctypes.byref(res), None) == \
+    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, 0, ctypes.byref(kout), ctypes.byref(res), None) == \
         mxa.ERR_UNSUPPORTED
     # shapes differ
     res2 = _mx(s=65)
-    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, ctypes.byref(out), ctypes.byref(res2), None) == \
+    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, 0, ctypes.byref(out), ctypes.byref(res2), None) == \
         mxa.ERR_INVALID_ARG
     # null residual descriptor
-    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, ctypes.byref(out), None, None) == mxa.ERR_INVALID_ARG
+    assert lib.mxattn_quantize_dual(x, 2, strides, None, 0, 7.25, 0, ctypes.byref(out), None, None) == mxa.ERR_INVALID_ARG
 
 
 def test_select_rejects():

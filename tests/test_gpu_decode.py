@@ -11,7 +11,7 @@ import torch
 
 import bit_microscaled_flashattention_amd as mxa
 import synth
-from oracle import attention, mx, select
+from oracle import attention, mx, rotate, select
 from tests.helpers import assert_codes_equal, head_slice, host_f64, oracle_dequant, oracle_quantize
 
 pytestmark = pytest.mark.gpu
@@ -133,6 +133,50 @@ def test_decode_dual_residual_query():
     err_s = np.mean([np.abs(os_[bb, h] - ref_exact[(bb, h)]).mean() for (bb, h) in ref_exact])
     print(f"  mean |out - out(exact q)|: single {err_s:.3e}, dual {err_d:.3e}", flush=True)
     assert err_d < err_s / 2
+
+
+def test_decode_hadamard_rotated_query_and_keys():
+    """Query and K cache rotated by the Walsh-Hadamard transform before
+    MXFP4 (V as is): cache codes bit-exact with the oracle's float32
+    transform, decode parity on the rotated operands, and outputs closer to
+    attention on the unquantised inputs than without the rotation when K
+    has outlier channels."""
+    g = torch.Generator(device=DEV).manual_seed(37)
+    b, hq, hkv, tcap, d = 2, 8, 2, 1300, 128
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV)
+    k[:, :, :, 7] *= 12
+    k[:, :, :, 70] *= 12
+    k = k.to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([1300, 777], dtype=torch.int32, device=DEV)
+    print("decode with rotated query and keys", flush=True)
+    kc_r = mxa.quantize(k, "hd", hadamard=True)
+    qh_r = mxa.quantize(q[:, :, None, :], "hd", hadamard=True)
+    kc, vc = _cache(k, v)
+    out_r, lse_r = mxa.decode(qh_r, kc_r, vc, ctx, split_len=512, return_lse=True)
+    out_p = mxa.decode(_query(q), kc, vc, ctx, split_len=512)
+    torch.cuda.synchronize()
+    k_rot = rotate.hadamard_f32(host_f64(k).astype(np.float32), axis=3).astype(np.float64)
+    q_rot = rotate.hadamard_f32(host_f64(q[:, :, None, :]).astype(np.float32), axis=3).astype(np.float64)
+    kcodes, kscales = oracle_quantize(k_rot, "hd")
+    assert_codes_equal(kc_r, kcodes, kscales, "rotated K cache")
+    qd = oracle_dequant(*oracle_quantize(q_rot, "hd"), "hd")[:, :, 0]
+    kd_all = oracle_dequant(kcodes, kscales, "hd")
+    ref, ref_exact = {}, {}
+    for bb in range(b):
+        for h in range(hq):
+            kv = h // (hq // hkv)
+            vd = oracle_dequant(*oracle_quantize(host_f64(v[bb:bb + 1, kv:kv + 1]), "hd"), "hd")[0, 0]
+            ref[(bb, h)] = attention.decode_head(qd[bb, h], kd_all[bb, kv], vd, int(ctx[bb]))
+            ref_exact[(bb, h)] = attention.decode_head(host_f64(q[bb, h]), host_f64(k[bb, kv]),
+                                                       host_f64(v[bb, kv]), int(ctx[bb]))[0]
+    _compare(out_r, lse_r, ref, "rotated decode")
+    orr, op = out_r.cpu().numpy(), out_p.cpu().numpy()
+    err_r = np.mean([np.abs(orr[bb, h] - ref_exact[(bb, h)]).mean() for (bb, h) in ref_exact])
+    err_p = np.mean([np.abs(op[bb, h] - ref_exact[(bb, h)]).mean() for (bb, h) in ref_exact])
+    print(f"  mean |out - exact|: plain {err_p:.3e}, rotated {err_r:.3e}", flush=True)
+    assert err_r < err_p
 
 
 def _hybrid_inputs(q, k, v, ctx, window, n_sel, max_sel, seed):

@@ -7,7 +7,7 @@ import torch
 
 import bit_microscaled_flashattention_amd as mxa
 import synth
-from oracle import mx, smooth
+from oracle import mx, rotate, smooth
 from tests.helpers import assert_codes_equal, host_f64, oracle_quantize
 
 pytestmark = pytest.mark.gpu
@@ -134,6 +134,35 @@ def test_quantize_dual_bit_exact(rule):
         q0 = mxa.quantize(xin.to(DEV), chan_scale=csin.to(DEV) if csin is not None else None, rule=rule)
         torch.cuda.synchronize()
         assert torch.equal(q0.codes, q1.codes) and torch.equal(q0.scales, q1.scales)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_quantize_hadamard_bit_exact(d, rule):
+    """Rotated rows (float32 transform in the documented order) give the
+    oracle's codes bit for bit, with channel factors and also through the
+    dual-residual split; fp32 input too."""
+    g = torch.Generator().manual_seed(61)
+    x = (torch.randn((2, 3, 45, d), generator=g) * 2).to(torch.bfloat16)
+    x[:, :, :, 3] *= 30
+    cs = torch.exp(torch.randn((3, d), generator=g)).to(torch.float32)
+    xf = torch.randn((1, 2, 33, d), generator=g) * 1e-3
+    r = mx.RULE_OCP if rule == "ocp" else mx.RULE_UOS
+    for xin, csin, what in ((x, cs, "bf16 with channel factors"), (xf, None, "fp32")):
+        print(f"quantize hadamard d={d} {rule} {what}", flush=True)
+        cd = csin.to(DEV) if csin is not None else None
+        got = mxa.quantize(xin.to(DEV), chan_scale=cd, rule=rule, hadamard=True)
+        q1, q2 = mxa.quantize_dual(xin.to(DEV), chan_scale=cd, rule=rule, hadamard=True)
+        torch.cuda.synchronize()
+        x32 = host_f64(xin).astype(np.float32)
+        if csin is not None:
+            x32 = smooth.apply(x32, csin.numpy())
+        xr = rotate.hadamard_f32(x32, axis=3).astype(np.float64)
+        oc, os_ = oracle_quantize(xr, "hd", r)
+        assert_codes_equal(got, oc, os_, f"rotated {what}")
+        c1, s1, c2, s2 = mx.quantize_dual(xr, axis=3, rule=r)
+        assert_codes_equal(q1, c1, s1, f"rotated dual first, {what}")
+        assert_codes_equal(q2, c2, s2, f"rotated dual residual, {what}")
 
 
 def _batch_case(seed=21):
