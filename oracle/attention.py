@@ -36,6 +36,18 @@ Readings
   * Causal masking (Sq == Sk only): key t is visible to query i iff t <= i.
   * l_from_quantized=True is the PNQ / P-Reordering normaliser (l = sum P_hat);
     False is the baseline that sums the unquantised exponentials.
+  * Hybrid prefill (HyQuant: in prefill the 4-bit and the full-precision
+    tokens share one FlashAttention kernel and one online softmax).  Query i
+    uses the full-precision rows for its ``window`` most recent keys
+    (i - window < t <= i) and for the selected vertical-line keys t <= i;
+    every other visible key takes the 4-bit path.  The page fixes neither the
+    prefill window nor the order of the two parts; the reading is a window
+    that slides with the query (the decode window is the last tokens of the
+    context) and the 4-bit tiles first, with the full-precision keys removed
+    from them (they contribute 0 and never raise a P block maximum), then
+    one update over all full-precision keys with P unquantised (l adds the
+    unquantised exponentials).  So no 4-bit P quantisation decision depends
+    on a full-precision logit.
   * Decode does not quantise P (none of the sources gives a decode P format; the
     cache's V blocks run along head_dim, so a 4-bit PV contraction over keys
     has no block scales to use).
@@ -46,7 +58,11 @@ tile wider than the sequence it equals a direct whole-row PNQ computation;
 the effective weights are non-negative and sum to one per row; l >= 1; the
 smoothing rescale is output-neutral; decode equals the prefill path on the
 same operands; hybrid decode reduces to pure-FP4 and to pure-BF16 attention
-in its two limits.  Attention values under quantisation have no worked
+in its two limits; hybrid prefill reduces to the 4-bit prefill (empty set,
+window 0) and to textbook attention on the full-precision rows (window >= Sq),
+equals textbook attention for any window and set when P is not quantised and
+both operand sets coincide (every key counted once), and matches a direct
+whole-row computation when one tile spans the sequence.  Attention values under quantisation have no worked
 example in the sources: beyond those invariants they are "parity unpinned".
 """
 
@@ -127,11 +143,15 @@ def _envelope_tile(pt, ph, e, s, m_new, rule, qmax):
 def prefill_head(q, k, v, *, causal=False, softmax_scale=None, kv_tile=128,
                  quantize_p=True, p_rule=mx.RULE_OCP, p_qmax=mx.UOS_QMAX,
                  l_from_quantized=True, rows=None, envelope=False,
-                 return_weights=False, return_tile_eps=False, _perturb=None):
+                 return_weights=False, return_tile_eps=False, hybrid=None, _perturb=None):
     """One head of the tiled online-softmax forward pass.
 
     q: [Sq, D], k/v: [Sk, D] float64 (dequantised operands or raw values).
     rows: query rows to evaluate (default: all); rows are independent.
+    hybrid (causal only): dict with ``window`` (int >= 0), ``sel`` (selected
+    key positions; entries outside [0, Sk) are ignored) and the
+    full-precision rows ``q`` [Sq, D], ``k``, ``v`` [Sk, D]; see the module
+    readings for which keys use them.
     Returns a dict with out [R, D], lse [R], m [R], l [R] and, on request,
     bound [R] (the float32 rounding envelope), weights [R, Sk] (the effective
     normalised attention weights) and tile_eps [R, n_tiles] (sum P_hat /
@@ -149,6 +169,17 @@ def prefill_head(q, k, v, *, causal=False, softmax_scale=None, kv_tile=128,
     assert kv_tile % mx.BLOCK == 0
     rows = np.arange(sq) if rows is None else np.asarray(rows, dtype=np.int64)
     r = rows.shape[0]
+    if hybrid is not None:
+        if not causal:
+            raise ValueError("hybrid prefill is causal")
+        win = int(hybrid["window"])
+        assert win >= 0
+        sel = np.asarray(hybrid.get("sel", []), dtype=np.int64).reshape(-1)
+        in_sel = np.zeros(sk, dtype=bool)
+        in_sel[sel[(sel >= 0) & (sel < sk)]] = True
+        qf = np.asarray(hybrid["q"], dtype=np.float64)
+        kf = np.asarray(hybrid["k"], dtype=np.float64)
+        vf = np.asarray(hybrid["v"], dtype=np.float64)
     qr = q[rows]
     m = np.full(r, -np.inf)
     l = np.zeros(r)
@@ -164,6 +195,9 @@ def prefill_head(q, k, v, *, causal=False, softmax_scale=None, kv_tile=128,
         visible = np.ones((r, n), dtype=bool)
         if causal:
             visible = keys[None, :] <= rows[:, None]
+        if hybrid is not None:
+            # Keys held in full precision for a row leave its 4-bit tiles.
+            visible &= (keys[None, :] <= rows[:, None] - win) & ~in_sel[keys][None, :]
         act = visible.any(axis=1)
         if not act.any():
             continue
@@ -201,6 +235,24 @@ def prefill_head(q, k, v, *, causal=False, softmax_scale=None, kv_tile=128,
         if return_tile_eps:
             with np.errstate(invalid="ignore", divide="ignore"):
                 teps[ia, j] = ph.sum(axis=1) / pt.sum(axis=1) - 1.0
+    if hybrid is not None:
+        # One update with every full-precision key of each row, P unquantised.
+        keys = np.arange(sk)
+        hv = (keys[None, :] <= rows[:, None]) & ((keys[None, :] > rows[:, None] - win) | in_sel[None, :])
+        ia = np.nonzero(hv.any(axis=1))[0]
+        if ia.size:
+            vis = hv[ia]
+            s = softmax_scale * (qf[rows[ia]] @ kf.T)
+            m_old = m[ia]
+            m_new = np.maximum(m_old, np.where(vis, s, -np.inf).max(axis=1))
+            alpha = np.where(np.isfinite(m_old), np.exp(m_old - m_new), 0.0)
+            p = np.where(vis, np.exp(np.where(vis, s, 0.0) - m_new[:, None]), 0.0)
+            l[ia] = alpha * l[ia] + p.sum(axis=1)
+            o[ia] = alpha[:, None] * o[ia] + p @ vf
+            m[ia] = m_new
+            env[ia] = alpha * env[ia]
+            if return_weights:
+                wts[ia] = wts[ia] * alpha[:, None] + p
     with np.errstate(invalid="ignore", divide="ignore"):
         out = o / l[:, None]
         lse = m + np.log(l)

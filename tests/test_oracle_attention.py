@@ -3,7 +3,8 @@
 The oracle is checked against textbook softmax attention (quantisation off),
 a direct whole-row PNQ computation (tile wider than the sequence), the
 normalisation invariant PNQ guarantees, the output-neutrality of Smooth-QK,
-and the limits of hybrid decode.  A planted float32-sized perturbation of
+and the limits of hybrid decode and prefill (with a closed-form key count for
+the window and the selected set).  A planted float32-sized perturbation of
 the exponentials checks that the rounding envelope covers what it claims.
 """
 
@@ -252,3 +253,101 @@ def test_envelope_flags_and_covers_midpoints_and_scale_boundaries(rule):
         moved = max(moved, diff)
         assert diff <= ref["bound"][0] + 1e-12
     assert moved > 1e-4        # the planted flips really changed the result
+
+
+# ---------------------------------------------------------------- hybrid prefill
+def _hy(qf, kf, vf, window, sel):
+    return {"window": window, "sel": np.asarray(sel, dtype=np.int64), "q": qf, "k": kf, "v": vf}
+
+
+def test_hybrid_prefill_key_counts_closed_form():
+    """All logits 0 (uniform weights) and a marker channel that is 1 only in
+    the full-precision V rows: out[i, 0] = |full-precision keys of row i| /
+    (i + 1), with i - W < t <= i the window and selected keys t <= i."""
+    s, d, win, sel = 60, 32, 3, [2, 11, 40, 59]
+    z = np.zeros((s, d))
+    v4 = np.zeros((s, d))
+    vf = np.zeros((s, d))
+    vf[:, 0] = 1.0
+    res = attention.prefill_head(z, z, v4, causal=True, kv_tile=32, quantize_p=False,
+                                 hybrid=_hy(z, z, vf, win, sel))
+    for i in range(s):
+        n_win = min(win, i + 1)
+        n_sel = sum(1 for t in sel if t <= i - win)
+        assert res["out"][i, 0] == pytest.approx((n_win + n_sel) / (i + 1), abs=1e-14), i
+
+
+def test_hybrid_prefill_limits():
+    """Empty set and window 0: the 4-bit prefill, bit for bit.  Window >= Sq:
+    textbook attention on the full-precision rows."""
+    q, k, v = _rand((150, 64), 31) * 2, _rand((150, 64), 32), _rand((150, 64), 33)
+    qf, kf, vf = _rand((150, 64), 34), _rand((150, 64), 35), _rand((150, 64), 36)
+    plain = attention.prefill_head(q, k, v, causal=True, kv_tile=64)
+    hyb0 = attention.prefill_head(q, k, v, causal=True, kv_tile=64, hybrid=_hy(qf, kf, vf, 0, []))
+    assert np.array_equal(plain["out"], hyb0["out"]) and np.array_equal(plain["lse"], hyb0["lse"])
+    allf = attention.prefill_head(q, k, v, causal=True, kv_tile=64, hybrid=_hy(qf, kf, vf, 150, [3, 77]))
+    np.testing.assert_allclose(allf["out"], _textbook(qf, kf, vf, True, 1 / 8), atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_tile", [32, 64, 128])
+@pytest.mark.parametrize("win, sel", [(0, [0, 5, 63, 64, 150]), (16, []), (40, [1, 2, 3, 100, 190]),
+                                      (7, list(range(0, 200, 9)))])
+def test_hybrid_prefill_quantisation_off_equals_textbook(kv_tile, win, sel):
+    """With P unquantised and one operand set for both paths, splitting keys
+    between the parts must leave textbook attention unchanged: a key counted
+    twice or dropped fails."""
+    q, k, v = _rand((200, 64), 37), _rand((200, 64), 38), _rand((200, 64), 39)
+    res = attention.prefill_head(q, k, v, causal=True, kv_tile=kv_tile, quantize_p=False,
+                                 hybrid=_hy(q, k, v, win, sel))
+    np.testing.assert_allclose(res["out"], _textbook(q, k, v, True, 1 / 8), atol=1e-12)
+
+
+def _direct_hybrid(q, k, v, qf, kf, vf, win, sel, scale, rule, qmax):
+    """Whole-row hybrid PNQ written out per row: the 4-bit keys' exponentials
+    against their own maximum, quantised in 32-key blocks from key 0, then
+    the full-precision keys rescaled into the same softmax."""
+    sq = q.shape[0]
+    sel = set(sel)
+    out = np.zeros((sq, v.shape[1]))
+    for i in range(sq):
+        f4 = [t for t in range(i + 1) if t <= i - win and t not in sel]
+        hf = [t for t in range(i + 1) if t > i - win or t in sel]
+        s4 = scale * (k[f4] @ q[i]) if f4 else np.zeros(0)
+        sf = scale * (kf[hf] @ qf[i])
+        m4 = s4.max() if f4 else -np.inf
+        m = max(m4, sf.max())
+        o = np.zeros(v.shape[1])
+        l = 0.0
+        if f4:
+            row = np.zeros(-(-sq // 32) * 32)
+            row[f4] = np.exp(s4 - m4)
+            codes, sb = mx.quantize_blocks(row[None], rule, qmax)
+            ph = mx.dequantize_blocks(codes, sb)[0, :sq]
+            o += np.exp(m4 - m) * (ph @ v[:sq])
+            l += np.exp(m4 - m) * ph.sum()
+        pf = np.exp(sf - m)
+        o += pf @ vf[hf]
+        l += pf.sum()
+        out[i] = o / l
+    return out
+
+
+@pytest.mark.parametrize("rule", [mx.RULE_OCP, mx.RULE_UOS])
+def test_hybrid_prefill_single_tile_equals_direct(rule):
+    q, k, v = _rand((96, 64), 40) * 2, _rand((96, 64), 41), _rand((96, 64), 42)
+    qf, kf, vf = q + 0.1 * _rand((96, 64), 43), k + 0.1 * _rand((96, 64), 44), v + 0.1 * _rand((96, 64), 45)
+    win, sel = 10, [0, 4, 30, 31, 70, 95]
+    res = attention.prefill_head(q, k, v, causal=True, kv_tile=128, p_rule=rule,
+                                 hybrid=_hy(qf, kf, vf, win, sel))
+    np.testing.assert_allclose(res["out"], _direct_hybrid(q, k, v, qf, kf, vf, win, sel, 1 / 8, rule, 7.25),
+                               atol=1e-12)
+
+
+def test_hybrid_prefill_weights_normalised():
+    q, k, v = _rand((130, 64), 46) * 2, _rand((130, 64), 47), _rand((130, 64), 48)
+    res = attention.prefill_head(q, k, v, causal=True, kv_tile=32, return_weights=True,
+                                 hybrid=_hy(q * 1.01, k, v, 20, [5, 6, 64, 100]))
+    w = res["weights"]
+    assert (w >= 0).all()
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(np.triu(w, 1) == 0)
