@@ -143,12 +143,44 @@ def prefill_leg(args):
     wall, kern = timed(step, args.steps, args.warmup, attn)
     _, quant = timed(lambda: None, args.steps, 0, lambda: mxa.quantize_batch(qkv_jobs))
     wall_r, quant_r = timed(step_rot, args.steps, args.warmup, lambda: mxa.quantize_batch(rot_jobs))
+    # Hybrid prefill: the top 5% vertical-line keys by column mass of the last
+    # 64 queries, and a 128-key window per row, in bf16 (selection untimed
+    # here, timed on its own).
+    W = 128
+    ctx = torch.tensor([S], dtype=torch.int32, device="cuda")
+    col = torch.zeros((B, HKV, S), dtype=torch.float32, device="cuda")
+    qr = mxa.quantize(d["q"][:, :, S - 64:], "hd")
+    step()
+    sel_ws = torch.empty(mxa.select_workspace_bytes(B, HQ, 64, S), dtype=torch.uint8, device="cuda")
+
+    def select():
+        col.zero_()
+        return mxa.select_vertical(qr, kh, ctx, col, window=W, workspace=sel_ws)
+
+    idx, nsel = select()
+
+    def attn_h():
+        mxa.prefill_hybrid(qh, kh, vh, d["q"], d["k"], d["v"], W, idx, nsel, kv_tile=args.kv_tile, out=out)
+
+    def step_h():
+        mxa.quantize_batch(qkv_jobs)
+        attn_h()
+
+    wall_h, kern_h = timed(step_h, args.steps, args.warmup, attn_h)
+    _, sel_t = timed(lambda: None, args.steps, 0, select)
     pairs = B * HQ * S * (S + 1) // 2
     flops = 4 * D * pairs
     res = {
         "flops": flops, "step_s": wall, "kernel_s": kern,
         "step_tflops": flops / wall / 1e12, "kernel_tflops": flops / kern / 1e12,
         "quantize_s": quant,
+        "hybrid_prefill": {"ms_per_step": round(wall_h * 1e3, 4), "kernel_ms": round(kern_h * 1e3, 4),
+                           "kernel_tflops": round(flops / kern_h / 1e12, 2),
+                           "selection_ms": round(sel_t * 1e3, 4),
+                           "n_sel_per_kv_head": int(nsel.max().item()), "window": W,
+                           "note": "vertical-line keys (top 5% column mass of the last 64 queries over the "
+                                   "non-window prefix) and a 128-key sliding window per row in bf16 under the "
+                                   "same softmax; flops counted as for the 4-bit step"},
         "hadamard_qk": {"ms_per_step": round(wall_r * 1e3, 4), "step_tflops": round(flops / wall_r / 1e12, 2),
                         "quantize_ms": round(quant_r * 1e3, 4), "plain_quantize_ms": round(quant * 1e3, 4),
                         "note": "Q and K rows rotated by the normalised Walsh-Hadamard transform before MXFP4 "
@@ -397,6 +429,7 @@ def main():
                      "kernel_ms": round(pre["kernel_s"] * 1e3, 4),
                      "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,true,true>")},
         "hadamard_qk": pre["hadamard_qk"],
+        "hybrid_prefill": pre["hybrid_prefill"],
     }
     del d
     torch.cuda.empty_cache()

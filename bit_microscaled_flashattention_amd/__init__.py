@@ -66,6 +66,14 @@ class _PrefillParams(ctypes.Structure):
     ]
 
 
+class _PrefillHybrid(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("idx", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
+        ("max_sel", ctypes.c_int32), ("window", ctypes.c_int32),
+    ]
+
+
 class _Hybrid(ctypes.Structure):
     _fields_ = [
         ("idx", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
@@ -86,6 +94,7 @@ def _load():
         "mxattn_quantize_batch": [P(_QuantJob), i32, vp],
         "mxattn_smooth_calibrate": [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp],
         "mxattn_prefill": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), vp, i32, vp, vp],
+        "mxattn_prefill_hybrid": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), P(_PrefillHybrid), vp, i32, vp, vp],
         "mxattn_decode": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
         "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, i32, P(_Mx), P(_Mx), vp],
         "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
@@ -111,6 +120,7 @@ _lib = _load()
 # Every symbol the C header declares (checked by the CPU tests).
 EXPORTS = (
     "mxattn_quantize", "mxattn_quantize_dual", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
+    "mxattn_prefill_hybrid",
     "mxattn_decode_workspace_bytes", "mxattn_decode",
     "mxattn_select_workspace_bytes", "mxattn_select_vertical",
     "mxattn_status_string", "mxattn_last_error", "mxattn_version",
@@ -277,6 +287,34 @@ def prefill(q, k, v, causal=False, softmax_scale=0.0, kv_tile=128, p_rule="ocp",
     dq, dk, dv = q.desc(), k.desc(), v.desc()
     _check(_lib.mxattn_prefill(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(p),
                                _ptr(out), _DT[out.dtype], _ptr(lse), _stream(q.codes)))
+    return (out, lse) if return_lse else out
+
+
+def prefill_hybrid(q, k, v, q_bf16, k_bf16, v_bf16, window, idx=None, n_sel=None, softmax_scale=0.0,
+                   kv_tile=128, p_rule="ocp", p_qmax=UOS_QMAX, l_from_quantized=True,
+                   out_dtype=torch.float32, return_lse=False, out=None):
+    """Causal prefill with per-row bf16 keys under one softmax: the window of
+    each query row and the selected keys idx [B,Hkv,max_sel] (ascending, the
+    first n_sel [B,Hkv] of each row used) take the bf16 rows q_bf16
+    [B,Hq,S,D], k_bf16/v_bf16 [B,Hkv,S,D]; every other key the MXFP4 path."""
+    b, hq, sq, d = q.shape
+    for t in (q_bf16, k_bf16, v_bf16):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous(), "bf16 rows must be contiguous bfloat16"
+    if out is None:
+        out = torch.empty((b, hq, sq, d), dtype=out_dtype, device=q.codes.device)
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.codes.device) if return_lse else None
+    p = _PrefillParams(1, float(softmax_scale), int(kv_tile), _RULES[p_rule], float(p_qmax),
+                       int(bool(l_from_quantized)))
+    hy = _PrefillHybrid()
+    hy.q, hy.k, hy.v = q_bf16.data_ptr(), k_bf16.data_ptr(), v_bf16.data_ptr()
+    if idx is not None:
+        assert idx.dtype == torch.int32 and idx.is_contiguous(), "idx must be contiguous int32"
+        assert n_sel.dtype == torch.int32 and n_sel.is_contiguous(), "n_sel must be contiguous int32"
+        hy.idx, hy.n_sel, hy.max_sel = idx.data_ptr(), n_sel.data_ptr(), idx.shape[-1]
+    hy.window = int(window)
+    dq, dk, dv = q.desc(), k.desc(), v.desc()
+    _check(_lib.mxattn_prefill_hybrid(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(p),
+                                      ctypes.byref(hy), _ptr(out), _DT[out.dtype], _ptr(lse), _stream(q.codes)))
     return (out, lse) if return_lse else out
 
 

@@ -259,11 +259,10 @@ mxattn_status_t mxattn_smooth_calibrate(const void* q_cal, const void* k_cal, mx
   return after_launch(launch_smooth_calibrate(a, s), s, "smooth_calibrate");
 }
 
-mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
-                               const mxattn_prefill_params_t* p, void* out, mxattn_dtype_t out_dtype, float* lse,
-                               mxattn_stream_t stream) {
+static mxattn_status_t prefill_common(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
+                                      const mxattn_prefill_params_t* p, const mxattn_prefill_hybrid_t* hy,
+                                      void* out, mxattn_dtype_t out_dtype, float* lse, mxattn_stream_t stream) {
   mxattn_status_t st;
-  if (injected("prefill", &st)) return st;
   if ((st = check_mx(q, "prefill.q", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if ((st = check_mx(k, "prefill.k", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if ((st = check_mx(v, "prefill.v", MXATTN_LAYOUT_KEY)) != MXATTN_OK) return st;
@@ -285,6 +284,18 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
   if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale))
     return fail(MXATTN_ERR_INVALID_ARG, "prefill: softmax_scale must be finite and >= 0");
   if (!aligned16(out)) return fail(MXATTN_ERR_INVALID_ARG, "prefill: out not 16-byte aligned");
+  if (hy != nullptr) {
+    if (!p->causal) return fail(MXATTN_ERR_UNSUPPORTED, "prefill_hybrid: the hybrid prefill is causal");
+    if (q->seq > kHybMaxSeq)
+      return fail(MXATTN_ERR_UNSUPPORTED, "prefill_hybrid: sequence %lld above %d", (long long)q->seq, kHybMaxSeq);
+    if (hy->q == nullptr || hy->k == nullptr || hy->v == nullptr)
+      return fail(MXATTN_ERR_INVALID_ARG, "prefill_hybrid: null bf16 q/k/v");
+    if (!aligned16(hy->q) || !aligned16(hy->k) || !aligned16(hy->v))
+      return fail(MXATTN_ERR_INVALID_ARG, "prefill_hybrid: bf16 q/k/v not 16-byte aligned");
+    if (hy->window < 0 || hy->max_sel < 0) return fail(MXATTN_ERR_INVALID_ARG, "prefill_hybrid: negative window/max_sel");
+    if (hy->max_sel > 0 && (hy->idx == nullptr || hy->n_sel == nullptr))
+      return fail(MXATTN_ERR_INVALID_ARG, "prefill_hybrid: null idx/n_sel with max_sel > 0");
+  }
   const int64_t grid = ((q->seq + 127) / 128) * q->batch * q->heads;
   if (grid > 0x7FFFFFFF || q->seq > 0x7FFFFFFF || k->seq > 0x7FFFFFFF)
     return fail(MXATTN_ERR_UNSUPPORTED, "prefill: problem too large for one launch");
@@ -308,8 +319,36 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
   a.l_from_quantized = p->l_from_quantized != 0;
   a.n_qblk = static_cast<int>((q->seq + 127) / 128);
   a.one_scale = 127;
+  if (hy != nullptr) {
+    a.hybrid = 1;
+    a.qf = static_cast<const uint16_t*>(hy->q);
+    a.kf = static_cast<const uint16_t*>(hy->k);
+    a.vf = static_cast<const uint16_t*>(hy->v);
+    a.sel_idx = hy->idx;
+    a.sel_n = hy->n_sel;
+    a.max_sel = hy->max_sel;
+    a.window = hy->window;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(launch_prefill(a, static_cast<int>(q->dim), kv_tile, p->causal != 0, s), s, "prefill");
+  return after_launch(launch_prefill(a, static_cast<int>(q->dim), kv_tile, p->causal != 0, s), s,
+                      hy != nullptr ? "prefill_hybrid" : "prefill");
+}
+
+mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
+                               const mxattn_prefill_params_t* p, void* out, mxattn_dtype_t out_dtype, float* lse,
+                               mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("prefill", &st)) return st;
+  return prefill_common(q, k, v, p, nullptr, out, out_dtype, lse, stream);
+}
+
+mxattn_status_t mxattn_prefill_hybrid(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
+                                      const mxattn_prefill_params_t* p, const mxattn_prefill_hybrid_t* hy,
+                                      void* out, mxattn_dtype_t out_dtype, float* lse, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("prefill_hybrid", &st)) return st;
+  if (hy == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "prefill_hybrid: null hybrid set");
+  return prefill_common(q, k, v, p, hy, out, out_dtype, lse, stream);
 }
 
 static int64_t bf16_slots(int64_t hybrid_rows) { return hybrid_rows > 0 ? (hybrid_rows + kBf16Rows - 1) / kBf16Rows : 0; }

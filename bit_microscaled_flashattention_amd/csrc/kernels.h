@@ -79,7 +79,21 @@ struct PrefillArgs {
   int l_from_quantized;
   int n_qblk;           // query blocks of 128 rows
   int one_scale;        // 127, kept in a kernel argument so it stays a register value
+  // hybrid (causal only): bf16 rows [B][H][S][D] contiguous, selected keys
+  int hybrid;
+  const uint16_t* qf;
+  const uint16_t* kf;
+  const uint16_t* vf;
+  const int32_t* sel_idx;  // [B][Hkv][max_sel], ascending
+  const int32_t* sel_n;    // [B][Hkv]
+  int max_sel;
+  int window;
 };
+
+// Longest sequence of the hybrid prefill: the selected-key bitmap of a
+// workgroup lives in LDS (one bit per key).
+constexpr int kHybMaxSeq = 65536;
+constexpr int kHybSelWords = kHybMaxSeq / 32;
 
 struct DecodeArgs {
   MxView q, k, v;

@@ -29,6 +29,16 @@
 //   * K/V tiles are double-buffered in LDS (rows padded to avoid bank
 //     conflicts); the grid is ordered longest-first for causal masks and
 //     mapped so that each XCD works on whole KV heads.
+//
+// Hybrid variant (HyQuant page, prefill paragraph: the 4-bit tiles and the
+// full-precision vertical-line and window keys share one kernel and one
+// online softmax).  Query i keeps its `window` most recent keys and the
+// selected keys in bf16.  The 4-bit tiles run first with those keys masked
+// out (the window as a causal limit shifted by `window`, the selected keys
+// through a bitmap in LDS), so every P quantisation decision is that of the
+// plain kernel on the remaining keys.  Then the workgroup walks the bf16 keys
+// in chunks of 32 (its window range, then the selected list): S^T and
+// O^T += V^T P^T on the bf16 MFMA, P unquantised as hi + lo bf16 parts.
 #include <type_traits>
 
 #include "mx_device.h"
@@ -248,10 +258,42 @@ __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int
   hq = (pair % a.Hkv) * G + g;
 }
 
-template <int D, int BC, bool CAUSAL, bool LQ, bool PUOS>
+// LDS of one bf16 chunk of the hybrid pass (two of them, alternating): 32 K
+// rows, 32 V rows (row stride padded by 16 bytes) and the 32 key positions.
+template <int D>
+struct HybCfg {
+  static constexpr int ROW = 2 * D + 16;
+  static constexpr int V_OFF = 32 * ROW;
+  static constexpr int POS_OFF = 64 * ROW;
+  static constexpr int BYTES = POS_OFF + 32 * 4;
+  static constexpr int PB = 2 * D / 8;  // bytes of a row staged by each of 8 threads
+};
+
+// Key of the 32-key chunk held by MFMA row i of the bf16 S^T product: bits 2
+// and 3 of i swapped, so that lane half h, register r of the result is key
+// 16 (r / 8) + 8 h + r % 8 -- the B operand layout of the PV k-steps.
+__device__ __forceinline__ int hyb_key(int i) { return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__device__ __forceinline__ v16f mfma32_bf16(v4i a, v4i b, v16f c) {
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
+                                                  0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 x = static_cast<__bf16>(lo), y = static_cast<__bf16>(hi);
+  return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
+}
+
+template <int D, int BC, bool CAUSAL, bool LQ, bool PUOS, bool HYB>
 __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, BC>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  static_assert(!HYB || CAUSAL, "the hybrid kernel is causal");
+  constexpr int SMEM = (HYB && 2 * HybCfg<D>::BYTES > 2 * C::STAGE) ? 2 * HybCfg<D>::BYTES : 2 * C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  // Padded by 8 words: a tile reads the words of all its blocks at once
+  // (those past the last row belong to empty blocks and are never used).
+  __shared__ __attribute__((aligned(16))) uint32_t selmap[HYB ? kHybSelWords + 8 : 1];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, j = lane & 31, hh = lane >> 5;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -276,14 +318,20 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
     }
   }
 
+  // The 4-bit path sees key t of query row i iff t <= i - shift (causal);
+  // the hybrid kernel shifts the limit by its window.
+  const int shift = HYB ? a.window : 0;
   const int last_q = (q0 + kBR - 1 < a.Sq - 1) ? q0 + kBR - 1 : a.Sq - 1;
-  const int nt = CAUSAL ? last_q / BC + 1 : (a.Sk + BC - 1) / BC;
+  const int nt = HYB ? (last_q - shift < 0 ? 0 : (last_q - shift) / BC + 1)
+                     : (CAUSAL ? last_q / BC + 1 : (a.Sk + BC - 1) / BC);
   const int wave_last_q = (q0 + wave_s * 32 + 31 < a.Sq - 1) ? q0 + wave_s * 32 + 31 : a.Sq - 1;
-  const int my_nt = CAUSAL ? wave_last_q / BC + 1 : nt;
+  const int my_nt = HYB ? (wave_last_q - shift < 0 ? 0 : (wave_last_q - shift) / BC + 1)
+                        : (CAUSAL ? wave_last_q / BC + 1 : nt);
   const int wave_first_q = q0 + wave_s * 32;
-  // Smallest and largest query row of this wave (padding rows repeat Sq - 1).
-  const int lo_q = wave_first_q < a.Sq - 1 ? wave_first_q : a.Sq - 1;
-  const int hi_q = wave_last_q;
+  // Smallest and largest query row of this wave (padding rows repeat Sq - 1),
+  // moved down by the shift.
+  const int lo_q = (wave_first_q < a.Sq - 1 ? wave_first_q : a.Sq - 1) - shift;
+  const int hi_q = wave_last_q - shift;
 
   // E2M1 ones for the normaliser: a 16x16x128 A operand whose rows 0-7 sum
   // the k-groups of lanes 0-15 and 32-47 (queries 0-15 of both key blocks)
@@ -314,10 +362,28 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   for (int dt = 0; dt < C::DT; ++dt) O[dt] = v16f{};
   v4f L = v4f{0, 0, 0, 0};
 
+  if constexpr (HYB) {
+    // Bitmap of the selected keys below the workgroup's last row (the 4-bit
+    // tiles never reach further).
+    const int nw = (last_q + 1 + 31) >> 5;
+    for (int w = tid; w < nw; w += kThreads) selmap[w] = 0u;
+    __syncthreads();
+    const int pair = b * a.Hkv + hk;
+    int ns = a.max_sel > 0 ? a.sel_n[pair] : 0;
+    ns = ns < 0 ? 0 : (ns > a.max_sel ? a.max_sel : ns);
+    const int32_t* ix = a.sel_idx + static_cast<int64_t>(pair) * a.max_sel;
+    for (int i = tid; i < ns; i += kThreads) {
+      const int t = ix[i];
+      if (t >= 0 && t <= last_q) atomicOr(&selmap[t >> 5], 1u << (t & 31));
+    }
+  }
+
   const TileSrc src = make_tile_src<D>(a, b, hk);
   ScaleRegs<D, BC> sr;
-  issue_tile<D, BC>(src, 0, smem, sr, tid, wave_s);
-  store_scales<D, BC>(sr, smem, tid);
+  if (!HYB || nt > 0) {
+    issue_tile<D, BC>(src, 0, smem, sr, tid, wave_s);
+    store_scales<D, BC>(sr, smem, tid);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -333,6 +399,24 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
     if (jt + 1 < nt) issue_tile<D, BC>(src, t0 + BC, next, sr, tid, wave_s);
     auto tile = [&]() {
       const uint8_t* base = smem + (jt & 1) * C::STAGE;
+      // Selected-key bitmap words of the tile's key blocks, read before the
+      // operands so that waiting for them leaves those loads in flight.
+      uint32_t selw[C::KB];
+      if constexpr (HYB) {
+        if constexpr (C::KB >= 4) {
+#pragma unroll
+          for (int q4 = 0; q4 < C::KB / 4; ++q4) {
+            const v4i w4 = *reinterpret_cast<const v4i*>(selmap + (t0 >> 5) + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) selw[4 * q4 + e] = static_cast<uint32_t>(w4[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < C::KB; ++e) selw[e] = selmap[(t0 >> 5) + e];
+        }
+#pragma unroll
+        for (int e = 0; e < C::KB; ++e) selw[e] = __builtin_amdgcn_readfirstlane(selw[e]);
+      }
 
       // Key block kb of this tile is [tb, tb + 32), tb = t0 + 32 kb.  Against
       // this wave's 32 query rows it is fully visible, empty (skipped) or
@@ -357,11 +441,28 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
         for (int dc = 0; dc < C::DC; ++dc)
           acc = mfma32_fp4_sel(aop[dc], qop[dc], acc, ksw, (kb % C::KPD) * C::DC + dc, qsc[dc]);
         if (blk_masked(kb)) {
-          const int qlim = CAUSAL ? qrow : 0x7FFFFFFF;
+          const int qlim = CAUSAL ? qrow - shift : 0x7FFFFFFF;
 #pragma unroll
           for (int r2 = 0; r2 < 16; ++r2) {
             const int t = t0 + kb * 32 + 16 * hh + r2;
             if (t > qlim || t >= a.Sk) acc[r2] = -__builtin_huge_valf();
+          }
+        }
+        if constexpr (HYB) {
+          // Selected keys go to the bf16 pass.  Lane half hh holds keys
+          // 16 hh + r2 of the block, so the select of register r2 takes its
+          // lane mask from bits r2 (lanes 0-31) and 16 + r2 (lanes 32-63) of
+          // the block's bitmap word, built in scalar registers.
+          const uint32_t w = selw[kb];
+          if (w != 0u) {
+            const float ninf = -__builtin_huge_valf();
+#pragma unroll
+            for (int r2 = 0; r2 < 16; ++r2) {
+              const uint32_t lo = static_cast<uint32_t>(static_cast<int32_t>(w << (31 - r2)) >> 31);
+              const uint32_t hi = static_cast<uint32_t>(static_cast<int32_t>(w << (15 - r2)) >> 31);
+              const uint64_t lm = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+              acc[r2] = __builtin_amdgcn_inverse_ballot_w64(lm) ? ninf : acc[r2];
+            }
           }
         }
         return acc;
@@ -389,8 +490,12 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
         tmax = fmaxf(tmax, x);
       }
       const float m_new = fmaxf(m, tmax);
-      const float alpha = fast_exp2((m - m_new) * a.c);
-      const float mc = m_new * a.c;
+      // The hybrid kernel can meet rows with no 4-bit key yet (m_new = -inf):
+      // their state stays zero.
+      const bool none = HYB && m_new == -__builtin_huge_valf();
+      const float mref = none ? 0.0f : m_new;
+      const float alpha = none ? 1.0f : fast_exp2((m - m_new) * a.c);
+      const float mc = mref * a.c;
 
       // ---- rescale the accumulators (skipped when no row's maximum moved)
       if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
@@ -416,7 +521,7 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
           eb[h2] = 1;
           if (blk_empty(kb)) continue;
           v16f& p = S[kb];
-          const float scl = p_block_scale(fast_exp2((bm[kb] - m_new) * a.c), PUOS, p_thr);
+          const float scl = p_block_scale(fast_exp2((bm[kb] - mref) * a.c), PUOS, p_thr);
           eb[h2] = static_cast<int>(__float_as_uint(scl) >> 23);
 #pragma unroll
           for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(p[r], a.c, -mc));
@@ -466,17 +571,220 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   };
   // Leading tiles fully visible to every row of the workgroup: keys below
   // the first query row (causal) and below Sk.
-  const int full_keys = CAUSAL ? (q0 + 1 < a.Sk ? q0 + 1 : a.Sk) : a.Sk;
+  const int full_keys = HYB ? (q0 + 1 - shift < 0 ? 0 : q0 + 1 - shift)
+                            : (CAUSAL ? (q0 + 1 < a.Sk ? q0 + 1 : a.Sk) : a.Sk);
   const int n_full = full_keys / BC < nt ? full_keys / BC : nt;
   int jt = 0;
   for (; jt < n_full; ++jt) step(jt, std::true_type{});
   for (; jt < nt; ++jt) step(jt, std::false_type{});
 
+  // ---- hybrid: the bf16 keys, after every 4-bit tile, in chunks of 32.
+  float lb = 0.0f;  // their share of the normaliser (unquantised P)
+  if constexpr (HYB) {
+    using H = HybCfg<D>;
+    const int W = a.window;
+    const int pair = b * a.Hkv + hk;
+    // Chunks: the workgroup's window keys [w_lo, last_q], then the selected
+    // list up to the last entry some row uses (entries are ascending).
+    const int w_lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+    const int n_wc = W > 0 ? (last_q - w_lo + 32) / 32 : 0;
+    int ns = a.max_sel > 0 ? a.sel_n[pair] : 0;
+    ns = ns < 0 ? 0 : (ns > a.max_sel ? a.max_sel : ns);
+    const int32_t* ix = a.sel_idx + static_cast<int64_t>(pair) * a.max_sel;
+    const int sel_lim = last_q - W;  // a selected key above this is in the window of every row
+    // Chunks of the list whose first entry some row uses: a prefix, since
+    // the entries ascend, counted 64 chunks per ballot.
+    const int nct = (ns + 31) / 32;
+    int n_sc = 0;
+    for (int base = 0; base < nct; base += 64) {
+      const int l = base + lane;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(l < nct && ix[32 * l] <= sel_lim);
+      n_sc += __builtin_popcountll(bal);
+      if (bal != ~0ull) break;
+    }
+    const int n_ch = n_wc + n_sc;
+    // B operand of S^T: bf16 query row qrow, channels 16 st + 8 hh .. +7.
+    v4i qb[D / 16];
+    if (n_ch > 0) {
+      const uint16_t* qsrc = a.qf + ((static_cast<int64_t>(b) * a.Hq + hq) * a.Sq + qrow) * D + 8 * hh;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) qb[st] = *reinterpret_cast<const v4i*>(qsrc + 16 * st);
+    }
+    const int slot = tid >> 3, part = tid & 7;
+    const uint16_t* kbase = a.kf + static_cast<int64_t>(pair) * a.Sk * D;
+    const uint16_t* vbase = a.vf + static_cast<int64_t>(pair) * a.Sk * D;
+    const int g16 = lane >> 4, s16 = lane & 15;
+    // This wave's rows (unshifted): a chunk none of them uses is skipped.
+    const int wq0 = lo_q + shift, wq1 = wave_last_q;
+
+    // Key position of this thread's slot in chunk ch (-1: empty slot).  A
+    // selected chunk's list entry is loaded one chunk ahead (sel_raw) and
+    // checked only when used, so the load stays in flight meanwhile.
+    auto sel_raw = [&](int ch) {
+      const int i = 32 * (ch - n_wc) + slot;
+      return i < ns ? ix[i] : -1;
+    };
+    auto slot_pos = [&](int ch, int raw) {
+      if (ch < n_wc) {
+        const int t = w_lo + 32 * ch + slot;
+        return t > last_q ? -1 : t;
+      }
+      return (raw < 0 || raw > sel_lim) ? -1 : raw;
+    };
+    // Rows of the next chunk travel in registers while the current one is
+    // computed (two LDS buffers, one barrier per chunk); the positions of the
+    // chunk after that are loaded one step earlier still.
+    v4i kv[H::PB / 16], vv[H::PB / 16];
+    int tpos = -1, tnext = -1;
+    auto fetch = [&]() {
+#pragma unroll
+      for (int u = 0; u < H::PB / 16; ++u) {
+        kv[u] = v4i{0, 0, 0, 0};
+        vv[u] = v4i{0, 0, 0, 0};
+      }
+      if (tpos >= 0) {
+        const uint8_t* ks = reinterpret_cast<const uint8_t*>(kbase + static_cast<int64_t>(tpos) * D) + part * H::PB;
+        const uint8_t* vs = reinterpret_cast<const uint8_t*>(vbase + static_cast<int64_t>(tpos) * D) + part * H::PB;
+#pragma unroll
+        for (int u = 0; u < H::PB / 16; ++u) {
+          kv[u] = *reinterpret_cast<const v4i*>(ks + 16 * u);
+          vv[u] = *reinterpret_cast<const v4i*>(vs + 16 * u);
+        }
+      }
+    };
+    if (n_ch > 0) {
+      tpos = slot_pos(0, n_wc == 0 ? sel_raw(0) : -1);
+      fetch();
+    }
+    if (n_ch > 1 && n_wc <= 1) tnext = sel_raw(1);
+    for (int ch = 0; ch < n_ch; ++ch) {
+      uint8_t* kl = smem + (ch & 1) * H::BYTES;
+      uint8_t* vl = kl + H::V_OFF;
+      int* pos = reinterpret_cast<int*>(kl + H::POS_OFF);
+#pragma unroll
+      for (int u = 0; u < H::PB / 16; ++u) {
+        *reinterpret_cast<v4i*>(kl + slot * H::ROW + part * H::PB + 16 * u) = kv[u];
+        *reinterpret_cast<v4i*>(vl + slot * H::ROW + part * H::PB + 16 * u) = vv[u];
+      }
+      if (part == 0) pos[slot] = tpos;
+      __syncthreads();
+      if (ch + 1 < n_ch) {
+        tpos = slot_pos(ch + 1, tnext);
+        fetch();
+      }
+      if (ch + 2 < n_ch && ch + 2 >= n_wc) tnext = sel_raw(ch + 2);
+
+      // Skip a chunk no row of this wave uses; drop the per-element mask
+      // when every row uses every key of it.
+      const bool win_chunk = ch < n_wc;
+      bool used, every;
+      if (win_chunk) {
+        const int c0 = w_lo + 32 * ch;
+        used = c0 <= wq1 && c0 + 31 > wq0 - W;
+        every = c0 > wq1 - W && c0 + 31 <= wq0;
+      } else {
+        // Slot 0 holds the smallest entry, slot 31 the largest (-1: empty).
+        const int f = pos[0], lst = pos[31];
+        used = f < 0 || f <= wq1 - W;
+        every = f >= 0 && lst >= 0 && lst <= wq0 - W;
+      }
+      if (!used) continue;
+
+      // S^T = K Q^T: lane (query j, half hh), register r is key 16(r/8) + 8hh + r%8.
+      const uint8_t* krow = kl + hyb_key(j) * H::ROW + 16 * hh;
+      v16f sc = v16f{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        sc = mfma32_bf16(*reinterpret_cast<const v4i*>(krow + 32 * st), qb[st], sc);
+      const v4i pa = *reinterpret_cast<const v4i*>(pos + 8 * hh);
+      const v4i pb = *reinterpret_cast<const v4i*>(pos + 8 * hh + 4);
+      const v4i pc = *reinterpret_cast<const v4i*>(pos + 16 + 8 * hh);
+      const v4i pd = *reinterpret_cast<const v4i*>(pos + 16 + 8 * hh + 4);
+      const int tk[16] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3],
+                          pc[0], pc[1], pc[2], pc[3], pd[0], pd[1], pd[2], pd[3]};
+      if (!every) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tt = tk[r];
+          const bool ok = tt >= 0 && tt <= qrow && (win_chunk ? tt > qrow - W : tt <= qrow - W);
+          if (!ok) sc[r] = -__builtin_huge_valf();
+        }
+      }
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float m_new = fmaxf(m, mx);
+      const bool none = m_new == -__builtin_huge_valf();
+      const float alpha = none ? 1.0f : fast_exp2((m - m_new) * a.c);
+      const float mc = none ? 0.0f : m_new * a.c;
+      float pv[16];
+      float ps = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pv[r] = fast_exp2(__builtin_fmaf(sc[r], a.c, -mc));
+        ps += pv[r];
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+        ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) O[dt] *= alpha;
+        L[0] *= __shfl(alpha, l_query);
+        if (!LQ) lsum *= alpha;
+      }
+      lb = lb * alpha + ps;
+      m = m_new;
+
+      // P^T as hi + lo bf16 B operands, k-step st = keys 16 st + 8 hh .. +7.
+      v4i bhi[2], blo[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        uint32_t h4[4], l4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = pv[8 * st + 2 * i], x1 = pv[8 * st + 2 * i + 1];
+          h4[i] = pack_bf16x2(x0, x1);
+          l4[i] = pack_bf16x2(x0 - __uint_as_float(h4[i] << 16), x1 - __uint_as_float(h4[i] & 0xFFFF0000u));
+        }
+        bhi[st] = v4i{(int)h4[0], (int)h4[1], (int)h4[2], (int)h4[3]};
+        blo[st] = v4i{(int)l4[0], (int)l4[1], (int)l4[2], (int)l4[3]};
+      }
+      // O^T += V^T P^T.  The A operand of lane (channel 32 dt + lane % 32,
+      // half hh) is V[16 st + 8 hh + 0..7][channel], read with the LDS
+      // transpose load: in each 16-lane group, lane 4a + b receives element
+      // b of the 8-byte reads of lanes a, a + 4, a + 8, a + 12, so lane s16
+      // reads channels 4 (s16 % 4) .. +3 of its group's 16 at key row
+      // s16 / 4 (then 4 rows on).
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef int v2i_t __attribute__((ext_vector_type(2)));
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint8_t* src = vl + (16 * st + 8 * hh + (s16 >> 2)) * H::ROW +
+                               2 * (32 * dt + 16 * (g16 & 1) + 4 * (s16 & 3));
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(src));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(src + 4 * H::ROW));
+          const v2i_t l2 = __builtin_bit_cast(v2i_t, lo), h2 = __builtin_bit_cast(v2i_t, hi);
+          const v4i aop = {l2[0], l2[1], h2[0], h2[1]};
+          O[dt] = mfma32_bf16(aop, bhi[st], O[dt]);
+          O[dt] = mfma32_bf16(aop, blo[st], O[dt]);
+        }
+    }
+  }
+
   // ---- finalise: out = O / l, lse = m * softmax_scale + ln l
   // The normaliser of query j sits in lane j (j < 16) or j + 16 (j >= 16).
   const float lq = __shfl(L[0], j < 16 ? j : j + 16);
   if (my_q >= a.Sq) return;
-  const float l = LQ ? lq : lsum;
+  const float l = (LQ ? lq : lsum) + (HYB ? lb : 0.0f);
   const float inv = 1.0f / l;
   const int64_t orow = (static_cast<int64_t>(b) * a.Hq + hq) * a.Sq + my_q;
   if (a.lse != nullptr && hh == 0) a.lse[orow] = m * a.softmax_scale + logf(l);
@@ -506,35 +814,41 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
 }
 
 template <int D, int BC, bool PUOS>
-static void launch_tp(const PrefillArgs& a, int causal, hipStream_t stream) {
+static void launch_tp(const PrefillArgs& a, int causal, bool hyb, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.n_qblk) * a.B * a.Hq;
   const bool lq = a.l_from_quantized != 0;
-  if (causal && lq)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, true, true, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
+  if (hyb && lq)
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, true, PUOS, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (hyb)
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, false, PUOS, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (causal && lq)
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, true, PUOS, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (causal)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, true, false, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, true, false, PUOS, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (lq)
-    hipLaunchKernelGGL((prefill_kernel<D, BC, false, true, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, false, true, PUOS, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BC, false, false, PUOS>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BC, false, false, PUOS, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       a);
 }
 
 template <int D, int BC>
-static void launch_t(const PrefillArgs& a, int causal, hipStream_t stream) {
-  if (a.p_uos) launch_tp<D, BC, true>(a, causal, stream);
-  else launch_tp<D, BC, false>(a, causal, stream);
+static void launch_t(const PrefillArgs& a, int causal, bool hyb, hipStream_t stream) {
+  if (a.p_uos) launch_tp<D, BC, true>(a, causal, hyb, stream);
+  else launch_tp<D, BC, false>(a, causal, hyb, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream) {
   if (a.n_qblk == 0) return hipSuccess;
+  const bool hyb = a.hybrid != 0;  // the caller checked causal
   if (D == 128) {
-    if (kv_tile == 64) launch_t<128, 64>(a, causal, stream);
-    else if (kv_tile == 128) launch_t<128, 128>(a, causal, stream);
-    else launch_t<128, 256>(a, causal, stream);
+    if (kv_tile == 64) launch_t<128, 64>(a, causal, hyb, stream);
+    else if (kv_tile == 128) launch_t<128, 128>(a, causal, hyb, stream);
+    else launch_t<128, 256>(a, causal, hyb, stream);
   } else {
-    if (kv_tile == 64) launch_t<64, 64>(a, causal, stream);
-    else if (kv_tile == 128) launch_t<64, 128>(a, causal, stream);
-    else launch_t<64, 256>(a, causal, stream);
+    if (kv_tile == 64) launch_t<64, 64>(a, causal, hyb, stream);
+    else if (kv_tile == 128) launch_t<64, 128>(a, causal, hyb, stream);
+    else launch_t<64, 256>(a, causal, hyb, stream);
   }
   return hipGetLastError();
 }

@@ -203,6 +203,42 @@ mxattn_status_t mxattn_prefill(const mxattn_mx_t* q, const mxattn_mx_t* k, const
                                mxattn_dtype_t out_dtype, float* lse, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * mxattn_prefill_hybrid -- causal mxattn_prefill in which each query row keeps
+ * some keys in bf16 under the same online softmax (HyQuant, prefill
+ * paragraph: the 4-bit and full-precision paths share one FlashAttention
+ * kernel and one softmax; vertical lines and a local window stay in full
+ * precision).
+ *   Query row i uses the bf16 rows for keys i - window < t <= i (its window,
+ *   itself included) and for the selected keys t <= i in idx[b][h][0..n_sel)
+ *   (strictly ascending; entries outside [0, S) are ignored; n_sel is
+ *   clamped to [0, max_sel] on the device).  Every other key t <= i takes
+ *   the MXFP4 path of mxattn_prefill.
+ *   Order: the MXFP4 tiles first, exactly as mxattn_prefill on the remaining
+ *   keys (the bf16 keys contribute 0 there and never raise a P block
+ *   maximum), then the bf16 keys: logits softmax_scale * (q_bf16 . k_bf16),
+ *   P unquantised (entering the bf16 MFMA as hi + lo parts), l += sum P.
+ *   q, k, v    MXFP4 operands as for mxattn_prefill (may be rotated or
+ *              smoothed; the bf16 rows are used as given).
+ *   hybrid->q  bf16 [B][Hq][S][D] contiguous; hybrid->k, ->v bf16
+ *              [B][Hkv][S][D] contiguous; all 16-byte aligned.
+ * Supported: params->causal = 1, S <= 65536, window >= 0, max_sel >= 0 (idx
+ * and n_sel may be NULL when max_sel = 0); otherwise as mxattn_prefill. */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;   /* [B][Hkv][max_sel] */
+  const int32_t* n_sel; /* [B][Hkv] */
+  int32_t max_sel;
+  int32_t window;
+} mxattn_prefill_hybrid_t;
+
+mxattn_status_t mxattn_prefill_hybrid(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
+                                      const mxattn_prefill_params_t* params,
+                                      const mxattn_prefill_hybrid_t* hybrid, void* out,
+                                      mxattn_dtype_t out_dtype, float* lse, mxattn_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * mxattn_decode -- one query token per sequence against an MXFP4 KV cache,
  * dequantisation fused into the scan, optionally with a bf16 hybrid token set
  * under the same softmax (HyQuant, method paragraphs).

@@ -102,6 +102,49 @@ def test_prefill_rejects(case, status):
     assert len(mxa.library().mxattn_last_error()) > 0
 
 
+@pytest.mark.parametrize("case, status", [
+    ("null_set", mxa.ERR_INVALID_ARG),
+    ("not_causal", mxa.ERR_UNSUPPORTED),
+    ("too_long", mxa.ERR_UNSUPPORTED),
+    ("null_rows", mxa.ERR_INVALID_ARG),
+    ("misaligned_rows", mxa.ERR_INVALID_ARG),
+    ("neg_window", mxa.ERR_INVALID_ARG),
+    ("neg_max_sel", mxa.ERR_INVALID_ARG),
+    ("null_idx", mxa.ERR_INVALID_ARG),
+    ("d96", mxa.ERR_UNSUPPORTED),
+])
+def test_prefill_hybrid_rejects(case, status):
+    """Argument checks of mxattn_prefill_hybrid, all taken before any launch."""
+    lib = mxa.library()
+    q, k, v = _mx(), _mx(), _mx(layout=1)
+    hy = mxa._PrefillHybrid()
+    hy.q, hy.k, hy.v = 4096, 8192, 12288
+    hy.idx, hy.n_sel, hy.max_sel, hy.window = 16384, 20480, 8, 64
+    causal = 1
+    if case == "not_causal":
+        causal = 0
+    elif case == "too_long":
+        q, k, v = _mx(s=65537), _mx(s=65537), _mx(s=65537, layout=1)
+    elif case == "null_rows":
+        hy.v = None
+    elif case == "misaligned_rows":
+        hy.k = 8200
+    elif case == "neg_window":
+        hy.window = -1
+    elif case == "neg_max_sel":
+        hy.max_sel = -2
+    elif case == "null_idx":
+        hy.idx = None
+    elif case == "d96":
+        q, k, v = _mx(d=96), _mx(d=96), _mx(d=96, layout=1)
+    p = mxa._PrefillParams(causal, 0.0, 128, 0, 7.25, 1)
+    st = lib.mxattn_prefill_hybrid(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(p),
+                                   None if case == "null_set" else ctypes.byref(hy),
+                                   ctypes.c_void_p(4096), 0, None, None)
+    assert st == status, mxa.library().mxattn_last_error()
+    assert len(mxa.library().mxattn_last_error()) > 0
+
+
 def test_quantize_rejects_without_launch():
     lib = mxa.library()
     out = _mx()

@@ -20,7 +20,7 @@ ATOL = 2e-3
 
 def _run_case(q, k, v, *, causal, kv_tile=128, p_rule="ocp", qkv_rule="ocp", l_from_quantized=True,
               rows=None, q_scale=None, k_scale=None, out_dtype=torch.float32, heads=None, what="",
-              hadamard=False):
+              hadamard=False, hybrid=None):
     """Quantise on the GPU, run prefill on every head, then check codes and
     outputs against the oracle on ``heads`` (query heads, default all) and
     ``rows`` (dict hq -> row indices, default all rows)."""
@@ -29,8 +29,14 @@ def _run_case(q, k, v, *, causal, kv_tile=128, p_rule="ocp", qkv_rule="ocp", l_f
     qh = mxa.quantize(q, "hd", chan_scale=q_scale, rule=qkv_rule, hadamard=hadamard)
     kh = mxa.quantize(k, "hd", chan_scale=k_scale, rule=qkv_rule, hadamard=hadamard)
     vh = mxa.quantize(v, "key", rule=qkv_rule)
-    out, lse = mxa.prefill(qh, kh, vh, causal=causal, kv_tile=kv_tile, p_rule=p_rule,
-                           l_from_quantized=l_from_quantized, out_dtype=out_dtype, return_lse=True)
+    if hybrid is None:
+        out, lse = mxa.prefill(qh, kh, vh, causal=causal, kv_tile=kv_tile, p_rule=p_rule,
+                               l_from_quantized=l_from_quantized, out_dtype=out_dtype, return_lse=True)
+    else:
+        assert causal
+        out, lse = mxa.prefill_hybrid(qh, kh, vh, q, k, v, hybrid["window"], hybrid.get("idx"),
+                                      hybrid.get("n_sel"), kv_tile=kv_tile, p_rule=p_rule,
+                                      l_from_quantized=l_from_quantized, out_dtype=out_dtype, return_lse=True)
     torch.cuda.synchronize()
     bsz, hq, _, _ = q.shape
     hkv = k.shape[1]
@@ -66,9 +72,17 @@ def _run_case(q, k, v, *, causal, kv_tile=128, p_rule="ocp", qkv_rule="ocp", l_f
         for i, h in enumerate(heads):
             kvi = kv_heads.index(h // grp)
             rr = None if rows is None else rows[h]
+            hy = None
+            if hybrid is not None:
+                kvh = h // grp
+                sel = np.zeros(0, dtype=np.int64)
+                if hybrid.get("idx") is not None:
+                    sel = hybrid["idx"][bi, kvh, :int(hybrid["n_sel"][bi, kvh])].cpu().numpy()
+                hy = {"window": hybrid["window"], "sel": sel, "q": host_f64(q[bi, h]),
+                      "k": host_f64(k[bi, kvh]), "v": host_f64(v[bi, kvh])}
             res = attention.prefill_head(qd[bi, i], kd[bi, kvi], vd[bi, kvi], causal=causal,
                                          kv_tile=kv_tile, p_rule=pr, l_from_quantized=l_from_quantized,
-                                         rows=rr, envelope=True)
+                                         rows=rr, envelope=True, hybrid=hy)
             g_rows = got[bi, h] if rr is None else got[bi, h][rr]
             l_rows = glse[bi, h] if rr is None else glse[bi, h][rr]
             worst = max(worst, check_within(g_rows, res["out"], res["bound"], atol, f"{what} b{bi} h{h}"))
@@ -208,3 +222,111 @@ def test_hadamard_rotation_cuts_error_on_key_outliers():
     e0, e1 = float(np.mean(err[False])), float(np.mean(err[True]))
     print(f"  mean |out - exact|: plain {e0:.3e}, rotated {e1:.3e}", flush=True)
     assert e1 < e0
+
+
+def _sel_sets(b, hkv, s, n, max_sel, seed, lo=0):
+    """Seeded ascending selected sets per (batch, KV head), -1 padded."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((b, hkv, max_sel), -1, dtype=np.int32)
+    nsel = np.zeros((b, hkv), dtype=np.int32)
+    for bi in range(b):
+        for h in range(hkv):
+            k = min(n, s - lo) if h % 2 == 0 else min(n // 2, s - lo)
+            pick = np.sort(rng.choice(np.arange(lo, s), size=k, replace=False))
+            idx[bi, h, :k] = pick
+            nsel[bi, h] = k
+    return torch.from_numpy(idx).to(DEV), torch.from_numpy(nsel).to(DEV)
+
+
+@pytest.mark.parametrize("d, kv_tile, window, n_sel", [
+    (128, 128, 64, 40), (128, 64, 200, 17), (128, 256, 1, 90), (64, 128, 130, 33), (128, 128, 0, 60),
+])
+def test_hybrid_prefill_parity(d, kv_tile, window, n_sel):
+    """bf16 window and selected keys after the 4-bit tiles, one softmax:
+    every row of a ragged multi-block case against the oracle."""
+    g = torch.Generator(device=DEV).manual_seed(70 + d + window)
+    b, hq, hkv, s = 2, 4, 2, 700
+    q = torch.randn((b, hq, s, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, s, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, s, d), generator=g, device=DEV).to(torch.bfloat16)
+    idx, nsel = _sel_sets(b, hkv, s, n_sel, 96, seed=window + n_sel)
+    _run_case(q, k, v, causal=True, kv_tile=kv_tile, hybrid={"window": window, "idx": idx, "n_sel": nsel},
+              what=f"hybrid d={d} tile={kv_tile} W={window} n={n_sel}")
+
+
+@pytest.mark.parametrize("p_rule, lq", [("uos", True), ("ocp", False)])
+def test_hybrid_prefill_rules_and_baseline_normaliser(p_rule, lq):
+    g = torch.Generator(device=DEV).manual_seed(77)
+    q = (torch.randn((1, 2, 333, 128), generator=g, device=DEV) * 1.5).to(torch.bfloat16)
+    k = torch.randn((1, 1, 333, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 1, 333, 128), generator=g, device=DEV).to(torch.bfloat16)
+    idx, nsel = _sel_sets(1, 1, 333, 25, 32, seed=3)
+    _run_case(q, k, v, causal=True, p_rule=p_rule, l_from_quantized=lq,
+              hybrid={"window": 48, "idx": idx, "n_sel": nsel}, what=f"hybrid p={p_rule} lq={lq}")
+
+
+def test_hybrid_prefill_limits():
+    """Window 0 and no selected keys: the plain kernel's output bit for bit.
+    Window >= S: attention on the bf16 rows alone (oracle, no 4-bit key)."""
+    g = torch.Generator(device=DEV).manual_seed(78)
+    q = torch.randn((1, 4, 300, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((1, 2, 300, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 2, 300, 128), generator=g, device=DEV).to(torch.bfloat16)
+    qh, kh, vh = mxa.quantize(q), mxa.quantize(k), mxa.quantize(v, "key")
+    plain, lp = mxa.prefill(qh, kh, vh, causal=True, return_lse=True)
+    empty = torch.zeros((1, 2, 4), dtype=torch.int32, device=DEV)
+    hy0, l0 = mxa.prefill_hybrid(qh, kh, vh, q, k, v, 0, empty, torch.zeros((1, 2), dtype=torch.int32, device=DEV),
+                                 return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, hy0) and torch.equal(lp, l0)
+    _run_case(q, k, v, causal=True, hybrid={"window": 300}, what="hybrid all-bf16 window")
+
+
+def test_hybrid_prefill_4k_gqa_selected_by_column_mass():
+    """The 4K causal GQA workload with the selection the decode side uses:
+    column mass of the last 64 queries over the non-window prefix, top 5%,
+    window 128; sampled rows of four heads against the oracle."""
+    d = synth.gqa_prefill(device=DEV)
+    S, W = 4096, 128
+    qh_recent = mxa.quantize(d["q"][:, :, S - 64:], "hd")
+    kh = mxa.quantize(d["k"], "hd")
+    ctx = torch.tensor([S], dtype=torch.int32, device=DEV)
+    col = torch.zeros((1, 8, S), dtype=torch.float32, device=DEV)
+    idx, n = mxa.select_vertical(qh_recent, kh, ctx, col, window=W)
+    torch.cuda.synchronize()
+    print(f"selected per KV head: {n.cpu().numpy().ravel().tolist()}", flush=True)
+    rng = np.random.default_rng(5)
+    heads = [0, 11, 22, 31]
+    rows = {h: np.unique(np.concatenate([[0, 1, 127, 128, 129, 4095], rng.integers(0, S, 40)])) for h in heads}
+    _run_case(d["q"], d["k"], d["v"], causal=True, heads=heads, rows=rows,
+              hybrid={"window": W, "idx": idx.contiguous(), "n_sel": n.contiguous()},
+              what="hybrid 4k gqa")
+
+
+def test_hybrid_prefill_cuts_error_on_heavy_columns():
+    """Keys that every query attends strongly (vertical lines) held in bf16:
+    the output moves towards float64 attention on the bf16 inputs."""
+    g = torch.Generator(device=DEV).manual_seed(79)
+    b, hq, hkv, s, dd = 1, 4, 2, 1024, 128
+    q = torch.randn((b, hq, s, dd), generator=g, device=DEV)
+    k = torch.randn((b, hkv, s, dd), generator=g, device=DEV)
+    heavy = torch.tensor([3, 100, 257, 600], device=DEV)
+    dirn = q.mean(dim=(1, 2))[:, None, :]            # a shared query direction
+    k[:, :, heavy] += 24.0 * dirn[:, :, None, :] / dirn.norm()
+    q = q + 2.0 * dirn[:, :, None, :] / dirn.norm()
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    v = torch.randn((b, hkv, s, dd), generator=g, device=DEV).to(torch.bfloat16)
+    qh, kh, vh = mxa.quantize(q), mxa.quantize(k), mxa.quantize(v, "key")
+    idx = heavy.to(torch.int32).repeat(b, hkv, 1).contiguous()
+    nsel = torch.full((b, hkv), 4, dtype=torch.int32, device=DEV)
+    plain = mxa.prefill(qh, kh, vh, causal=True).cpu().numpy()
+    hyb = mxa.prefill_hybrid(qh, kh, vh, q, k, v, 64, idx, nsel).cpu().numpy()
+    torch.cuda.synchronize()
+    e_p, e_h = [], []
+    for h in range(hq):
+        ref = attention.prefill_head(host_f64(q[0, h]), host_f64(k[0, h // 2]), host_f64(v[0, h // 2]),
+                                     causal=True, quantize_p=False)["out"]
+        e_p.append(np.abs(plain[0, h] - ref).mean())
+        e_h.append(np.abs(hyb[0, h] - ref).mean())
+    print(f"  mean |out - exact|: 4-bit {np.mean(e_p):.3e}, hybrid {np.mean(e_h):.3e}", flush=True)
+    assert np.mean(e_h) < 0.8 * np.mean(e_p)
