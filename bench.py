@@ -296,6 +296,31 @@ def decode_leg(args, flush):
     t_step = timed_flushed(step, args.steps, args.warmup, flush)
     t_call_d = timed_flushed(call_dual, args.steps, args.warmup, flush)
     t_step_d = timed_flushed(step_dual, args.steps, args.warmup, flush)
+
+    # The same cache as a shuffled pool of 64-token pages behind a block table.
+    PAGE = 64
+    maxp = T // PAGE
+    perm = torch.randperm(B * maxp, generator=torch.Generator().manual_seed(7))
+    table = perm.reshape(B, maxp).to(torch.int32).contiguous().cuda()
+
+    def to_pool(c):
+        def scatter(x):
+            src = x.reshape(B, HKV, maxp, PAGE, x.shape[-1]).permute(0, 2, 1, 3, 4).reshape(B * maxp, HKV, PAGE, -1)
+            dst = torch.empty_like(src)
+            dst[perm.cuda()] = src
+            return dst
+        return mxa.MX(scatter(c.codes), scatter(c.scales), (B * maxp, HKV, PAGE, D), "hd")
+
+    kp = to_pool(kc)
+    del kc
+    vp = to_pool(vc)
+    del vc
+    torch.cuda.empty_cache()
+
+    def call_paged():
+        mxa.decode_paged(qh, kp, vp, table, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
+
+    t_call_p = timed_flushed(call_paged, args.steps, args.warmup, flush)
     cache_bytes = B * HKV * T * (D // 2 + D // 32) * 2
     q_bytes = B * HQ * (D // 2 + D // 32)
     alg = cache_bytes + q_bytes + B * HQ * D * 4
@@ -318,6 +343,12 @@ def decode_leg(args, flush):
             "achieved_GB_per_s": round(alg_d / t_call_d / 1e9, 1),
             "frac": round(alg_d / t_call_d / 1e9 / PEAK_HBM_GBS, 4),
             "note": "q split into MXFP4(q) + MXFP4(q - dequant(MXFP4(q))); step = quantise both halves + decode",
+        },
+        "paged_kv": {
+            "call_ms": round(t_call_p * 1e3, 4),
+            "achieved_GB_per_s": round(alg / t_call_p / 1e9, 1),
+            "frac": round(alg / t_call_p / 1e9 / PEAK_HBM_GBS, 4),
+            "note": f"same cache as a shuffled pool of {PAGE}-token pages (block table [32, {maxp}])",
         },
     }
 

@@ -74,6 +74,10 @@ class _PrefillHybrid(ctypes.Structure):
     ]
 
 
+class _Paging(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32)]
+
+
 class _Hybrid(ctypes.Structure):
     _fields_ = [
         ("idx", ctypes.c_void_p), ("n_sel", ctypes.c_void_p),
@@ -96,6 +100,8 @@ def _load():
         "mxattn_prefill": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), vp, i32, vp, vp],
         "mxattn_prefill_hybrid": [P(_Mx), P(_Mx), P(_Mx), P(_PrefillParams), P(_PrefillHybrid), vp, i32, vp, vp],
         "mxattn_decode": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
+        "mxattn_decode_paged": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), P(_Paging), vp, P(_Hybrid), f32, i32, vp, sz,
+                                vp, vp, vp],
         "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, i32, P(_Mx), P(_Mx), vp],
         "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
     }
@@ -121,7 +127,7 @@ _lib = _load()
 EXPORTS = (
     "mxattn_quantize", "mxattn_quantize_dual", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
     "mxattn_prefill_hybrid",
-    "mxattn_decode_workspace_bytes", "mxattn_decode",
+    "mxattn_decode_workspace_bytes", "mxattn_decode", "mxattn_decode_paged",
     "mxattn_select_workspace_bytes", "mxattn_select_vertical",
     "mxattn_status_string", "mxattn_last_error", "mxattn_version",
 )
@@ -331,8 +337,25 @@ def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybr
     hybrid: None or dict(idx, n_sel, k_sel, v_sel, k_win, v_win, window).
     q_res: None or the residual MX of a dual-residual query (quantize_dual).
     """
+    return _decode(q, k_cache, v_cache, None, k_cache.shape[2], ctx_len, softmax_scale, split_len, hybrid,
+                   q_bf16, workspace, return_lse, out, q_res)
+
+
+def decode_paged(q, k_pool, v_pool, block_table, ctx_len, softmax_scale=0.0, split_len=2048, hybrid=None,
+                 q_bf16=None, workspace=None, return_lse=False, out=None, q_res=None):
+    """decode() over a paged cache: k_pool/v_pool MX [n_pages,Hkv,page_size,D],
+    block_table int32 [B,max_pages] (contiguous, on device) giving each
+    sequence's physical pages in order."""
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous(), "block_table must be contiguous int32"
+    pg = _Paging(block_table.data_ptr(), block_table.shape[1])
+    return _decode(q, k_pool, v_pool, pg, block_table.shape[1] * k_pool.shape[2], ctx_len, softmax_scale,
+                   split_len, hybrid, q_bf16, workspace, return_lse, out, q_res)
+
+
+def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, q_bf16, workspace, return_lse,
+            out, q_res):
     b, hq, _, d = q.shape
-    hkv, tcap = k_cache.shape[1], k_cache.shape[2]
+    hkv = kc.shape[1]
     dev = q.codes.device
     hy_rows = (hybrid["idx"].shape[-1] + int(hybrid["window"])) if hybrid is not None else 0
     need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hy_rows)
@@ -350,13 +373,15 @@ def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybr
         hy.k_sel, hy.v_sel = hybrid["k_sel"].data_ptr(), hybrid["v_sel"].data_ptr()
         hy.k_win = hybrid["k_win"].data_ptr() if hybrid.get("k_win") is not None else None
         hy.v_win = hybrid["v_win"].data_ptr() if hybrid.get("v_win") is not None else None
-    dq, dk, dv = q.desc(), k_cache.desc(), v_cache.desc()
+    dq, dk, dv = q.desc(), kc.desc(), vc.desc()
     dqr = q_res.desc() if q_res is not None else None
-    _check(_lib.mxattn_decode(ctypes.byref(dq), ctypes.byref(dqr) if dqr is not None else None,
-                              _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv),
-                              _ptr(ctx_len), ctypes.byref(hy) if hy is not None else None,
-                              float(softmax_scale), int(split_len), _ptr(workspace), workspace.numel(),
-                              _ptr(out), _ptr(lse), _stream(q.codes)))
+    common = (ctypes.byref(dqr) if dqr is not None else None, _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv))
+    tail = (_ptr(ctx_len), ctypes.byref(hy) if hy is not None else None, float(softmax_scale), int(split_len),
+            _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(q.codes))
+    if paging is None:
+        _check(_lib.mxattn_decode(ctypes.byref(dq), *common, *tail))
+    else:
+        _check(_lib.mxattn_decode_paged(ctypes.byref(dq), *common, ctypes.byref(paging), *tail))
     return (out, lse) if return_lse else out
 
 

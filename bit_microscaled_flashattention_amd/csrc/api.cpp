@@ -362,12 +362,12 @@ size_t mxattn_decode_workspace_bytes(int64_t batch, int64_t hq, int64_t hkv, int
   return bytes;
 }
 
-mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16, const mxattn_mx_t* kc,
-                              const mxattn_mx_t* vc, const int32_t* ctx_len, const mxattn_hybrid_t* hy,
-                              float softmax_scale, int32_t split_len, void* workspace, size_t workspace_bytes,
-                              float* out, float* lse, mxattn_stream_t stream) {
+static mxattn_status_t decode_common(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,
+                                     const mxattn_mx_t* kc, const mxattn_mx_t* vc, const mxattn_paging_t* pg,
+                                     const int32_t* ctx_len, const mxattn_hybrid_t* hy, float softmax_scale,
+                                     int32_t split_len, void* workspace, size_t workspace_bytes, float* out,
+                                     float* lse, mxattn_stream_t stream) {
   mxattn_status_t st;
-  if (injected("decode", &st)) return st;
   if ((st = check_mx(q, "decode.q", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if ((st = check_mx(kc, "decode.k_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if ((st = check_mx(vc, "decode.v_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
@@ -379,8 +379,23 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
       return fail(MXATTN_ERR_INVALID_ARG, "decode: q_res shape differs from q");
   }
   if (q->dim != kc->dim || kc->dim != vc->dim) return fail(MXATTN_ERR_INVALID_ARG, "decode: head_dim mismatch");
-  if (q->batch != kc->batch || kc->batch != vc->batch) return fail(MXATTN_ERR_INVALID_ARG, "decode: batch mismatch");
+  if (pg == nullptr && (q->batch != kc->batch || kc->batch != vc->batch))
+    return fail(MXATTN_ERR_INVALID_ARG, "decode: batch mismatch");
   if (kc->heads != vc->heads || kc->seq != vc->seq) return fail(MXATTN_ERR_INVALID_ARG, "decode: K/V cache shape mismatch");
+  // Token capacity per sequence: the cache length, or the block table's.
+  int64_t tcap = kc->seq;
+  if (pg != nullptr) {
+    if (kc->batch != vc->batch) return fail(MXATTN_ERR_INVALID_ARG, "decode_paged: K/V pools differ in pages");
+    if (pg->block_table == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode_paged: null block_table");
+    if (pg->max_pages < 1) return fail(MXATTN_ERR_INVALID_ARG, "decode_paged: max_pages must be >= 1");
+    const int64_t P = kc->seq;
+    if (P < 32 || P % 32 != 0) return fail(MXATTN_ERR_UNSUPPORTED, "decode_paged: page_size must be a multiple of 32");
+    if (split_len % P != 0 || split_len / P > 64)
+      return fail(MXATTN_ERR_UNSUPPORTED, "decode_paged: split_len must be a multiple of page_size, at most 64 pages");
+    if (kc->batch > 0x7FFFFFFF) return fail(MXATTN_ERR_UNSUPPORTED, "decode_paged: too many pages");
+    tcap = static_cast<int64_t>(pg->max_pages) * P;
+    if (tcap > 0x7FFFFFFF) return fail(MXATTN_ERR_UNSUPPORTED, "decode_paged: max_pages x page_size too large");
+  }
   if (q->heads % kc->heads != 0) return fail(MXATTN_ERR_INVALID_ARG, "decode: Hq %% Hkv != 0");
   const int64_t g = q->heads / kc->heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return fail(MXATTN_ERR_UNSUPPORTED, "decode: group size %lld", (long long)g);
@@ -399,14 +414,14 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
       return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid selected set pointers missing");
     if (hy->window > 0 && (!hy->k_win || !hy->v_win)) return fail(MXATTN_ERR_INVALID_ARG, "decode: hybrid window pointers missing");
     if (split_len > 8192) return fail(MXATTN_ERR_UNSUPPORTED, "decode: hybrid needs split_len <= 8192");
-    if (hy->max_sel + static_cast<int64_t>(hy->window) > kc->seq)
+    if (hy->max_sel + static_cast<int64_t>(hy->window) > tcap)
       return fail(MXATTN_ERR_INVALID_ARG, "decode: max_sel + window exceeds the cache");
   }
   const int64_t hybrid_rows = hybrid ? static_cast<int64_t>(hy->max_sel) + hy->window : 0;
-  const int64_t n_split = (kc->seq + split_len - 1) / split_len;
+  const int64_t n_split = (tcap + split_len - 1) / split_len;
   if (n_split + bf16_slots(hybrid_rows) > kMaxSlots)
     return fail(MXATTN_ERR_UNSUPPORTED, "decode: more than %lld partial slots; use a longer split_len", (long long)kMaxSlots);
-  const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, kc->seq, split_len,
+  const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, tcap, split_len,
                                                     static_cast<int32_t>(hybrid_rows));
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MXATTN_ERR_WORKSPACE, "decode: workspace of %zu bytes needed", need);
@@ -421,7 +436,14 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
   a.B = static_cast<int>(q->batch);
   a.Hq = static_cast<int>(q->heads);
   a.Hkv = static_cast<int>(kc->heads);
-  a.Tcap = static_cast<int>(kc->seq);
+  a.Tcap = static_cast<int>(tcap);
+  if (pg != nullptr) {
+    a.paged = 1;
+    a.block_table = pg->block_table;
+    a.max_pages = pg->max_pages;
+    a.page_size = static_cast<int>(kc->seq);
+    a.n_pages = static_cast<int>(kc->batch);
+  }
   const float sm = softmax_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(q->dim)) : softmax_scale;
   a.softmax_scale = sm;
   a.c = sm * 1.4426950408889634f;
@@ -444,7 +466,30 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
     a.v_win = static_cast<const uint16_t*>(hy->v_win);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return after_launch(launch_decode(a, static_cast<int>(q->dim), s), s, "decode");
+  return after_launch(launch_decode(a, static_cast<int>(q->dim), s), s, pg != nullptr ? "decode_paged" : "decode");
+}
+
+mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16, const mxattn_mx_t* kc,
+                              const mxattn_mx_t* vc, const int32_t* ctx_len, const mxattn_hybrid_t* hy,
+                              float softmax_scale, int32_t split_len, void* workspace, size_t workspace_bytes,
+                              float* out, float* lse, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("decode", &st)) return st;
+  return decode_common(q, q_res, q_bf16, kc, vc, nullptr, ctx_len, hy, softmax_scale, split_len, workspace,
+                       workspace_bytes, out, lse, stream);
+}
+
+mxattn_status_t mxattn_decode_paged(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,
+                                    const mxattn_mx_t* k_pool, const mxattn_mx_t* v_pool,
+                                    const mxattn_paging_t* paging, const int32_t* ctx_len,
+                                    const mxattn_hybrid_t* hybrid, float softmax_scale, int32_t split_len,
+                                    void* workspace, size_t workspace_bytes, float* out, float* lse,
+                                    mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("decode_paged", &st)) return st;
+  if (paging == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode_paged: null paging");
+  return decode_common(q, q_res, q_bf16, k_pool, v_pool, paging, ctx_len, hybrid, softmax_scale, split_len,
+                       workspace, workspace_bytes, out, lse, stream);
 }
 
 // Per (batch, query head, recent query, context chunk): partial (max, sum)

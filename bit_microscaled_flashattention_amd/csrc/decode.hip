@@ -234,7 +234,13 @@ constexpr int kMaxSplitWords = 8192 / 32;
 // only for that chunk's bytes.
 // DUAL: the query is a dual-residual pair (a.q, a.q2); each logit MFMA is
 // followed by one against the residual query, accumulating into it.
-template <int D, bool DUAL>
+// PAGED: the cache is a pool of pages of page_size tokens (BitDecoding-FP4,
+// "System-Level Optimization": paged KV cache with a block table).  A split
+// starts on a page boundary and spans at most 64 pages; each lane holds the
+// physical page of one of them, and a chunk (32 tokens, inside one page)
+// takes its page with a lane read and addresses it through resources built
+// on that page, so a bad table entry reads zeros instead of stray memory.
+template <int D, bool DUAL, bool PAGED>
 __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, uint32_t* selbits, int split,
                                           int hk, int b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -264,10 +270,22 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
     }
   }
   const int64_t kcs = a.k.cs[2], kss = a.k.ss[2], vcs = a.v.cs[2], vss = a.v.ss[2];
-  const __amdgpu_buffer_rsrc_t rkc = make_rsrc(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], uint32_t(t_end * kcs));
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1], uint32_t(t_end * kss));
-  const __amdgpu_buffer_rsrc_t rvc = make_rsrc(a.v.codes + b * a.v.cs[0] + hk * a.v.cs[1], uint32_t(t_end * vcs));
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v.scales + b * a.v.ss[0] + hk * a.v.ss[1], uint32_t(t_end * vss));
+  // Contiguous cache: one resource per operand over the split's (batch, KV
+  // head).  Paged: rebuilt per chunk from its page.
+  const int64_t bsel = PAGED ? 0 : b;
+  const __amdgpu_buffer_rsrc_t rkc0 = make_rsrc(a.k.codes + bsel * a.k.cs[0] + hk * a.k.cs[1], uint32_t(t_end * kcs));
+  const __amdgpu_buffer_rsrc_t rks0 = make_rsrc(a.k.scales + bsel * a.k.ss[0] + hk * a.k.ss[1], uint32_t(t_end * kss));
+  const __amdgpu_buffer_rsrc_t rvc0 = make_rsrc(a.v.codes + bsel * a.v.cs[0] + hk * a.v.cs[1], uint32_t(t_end * vcs));
+  const __amdgpu_buffer_rsrc_t rvs0 = make_rsrc(a.v.scales + bsel * a.v.ss[0] + hk * a.v.ss[1], uint32_t(t_end * vss));
+  int pg = -1;  // PAGED: physical page of the split's page `lane` (-1: none)
+  if constexpr (PAGED) {
+    const int np = a.split_len / a.page_size;
+    const int lp = t_begin / a.page_size + lane;
+    if (lane < np && lp < a.max_pages) {
+      const int e = a.block_table[static_cast<int64_t>(b) * a.max_pages + lp];
+      pg = (e >= 0 && e < a.n_pages) ? e : -1;
+    }
+  }
   uint8_t* vr = vstage + wave * kChunk * kVRow;
 
   DecState st;
@@ -278,12 +296,27 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
 
   constexpr int nblk_d = D / 32;
   auto load = [&](ChunkRegs& r, int t0) {
+    __amdgpu_buffer_rsrc_t rkc = rkc0, rks = rks0, rvc = rvc0, rvs = rvs0;
+    int tb = 0;  // token at offset 0 of the resources
+    if constexpr (PAGED) {
+      const int P = a.page_size;
+      int pi = (t0 - t_begin) / P;  // chunks past the split only meet out-of-range offsets
+      pi = pi < 63 ? pi : 63;
+      const int page = __builtin_amdgcn_readlane(pg, pi);
+      const int64_t pp = page >= 0 ? page : 0;
+      const uint32_t rec = page >= 0 ? 1u : 0u;
+      rkc = make_rsrc(a.k.codes + pp * a.k.cs[0] + hk * a.k.cs[1], rec * uint32_t(P * kcs));
+      rks = make_rsrc(a.k.scales + pp * a.k.ss[0] + hk * a.k.ss[1], rec * uint32_t(P * kss));
+      rvc = make_rsrc(a.v.codes + pp * a.v.cs[0] + hk * a.v.cs[1], rec * uint32_t(P * vcs));
+      rvs = make_rsrc(a.v.scales + pp * a.v.ss[0] + hk * a.v.ss[1], rec * uint32_t(P * vss));
+      tb = t_begin + pi * P;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = t0 + h * 16 + j;
       const bool ok = t < t_end && g < nblk_d;
-      const uint32_t oc = ok ? uint32_t(t * kcs + g * 16) : kOutOfRange;
-      const uint32_t os = ok ? uint32_t(t * kss + g) : kOutOfRange;
+      const uint32_t oc = ok ? uint32_t((t - tb) * kcs + g * 16) : kOutOfRange;
+      const uint32_t os = ok ? uint32_t((t - tb) * kss + g) : kOutOfRange;
       r.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rkc, oc, 0, kAuxStream);
       r.ks[h] = __builtin_amdgcn_raw_buffer_load_b8(rks, os, 0, 0);
     }
@@ -293,8 +326,8 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
       const int tt = bi / nblk_d, db = bi % nblk_d;
       const int t = t0 + tt;
       const bool ok = tt < kChunk && t < t_end;
-      const uint32_t oc = ok ? uint32_t(t * vcs + db * 16) : kOutOfRange;
-      const uint32_t os = ok ? uint32_t(t * vss + db) : kOutOfRange;
+      const uint32_t oc = ok ? uint32_t((t - tb) * vcs + db * 16) : kOutOfRange;
+      const uint32_t os = ok ? uint32_t((t - tb) * vss + db) : kOutOfRange;
       r.v[h] = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 0, kAuxStream);
       r.vs[h] = __builtin_amdgcn_raw_buffer_load_b8(rvs, os, 0, 0);
     }
@@ -486,12 +519,12 @@ __device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, 
 
 // One launch for the whole scan: blockIdx.x < n_split are the 4-bit splits,
 // the rest the bf16 hybrid parts, so the two kinds share the machine.
-template <int D, bool DUAL>
+template <int D, bool DUAL, bool PAGED>
 __global__ __launch_bounds__(kDecThreads, 3) void decode_scan_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
   __shared__ uint32_t selbits[kMaxSplitWords];
   if (static_cast<int>(blockIdx.x) < a.n_split)
-    fp4_split<D, DUAL>(a, vstage, selbits, blockIdx.x, blockIdx.y, blockIdx.z);
+    fp4_split<D, DUAL, PAGED>(a, vstage, selbits, blockIdx.x, blockIdx.y, blockIdx.z);
   else
     bf16_part<D>(a, vstage, blockIdx.x - a.n_split, blockIdx.y, blockIdx.z);
 }
@@ -545,19 +578,23 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   if (a.lse != nullptr && d == 0) a.lse[row] = s_m * a.softmax_scale + logf(s_den);
 }
 
+template <int D, bool DUAL>
+static void launch_scan(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.paged)
+    hipLaunchKernelGGL((decode_scan_kernel<D, DUAL, true>), grid, dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_scan_kernel<D, DUAL, false>), grid, dim3(kDecThreads), 0, stream, a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {
   const dim3 grid(a.n_split + (a.hybrid ? a.n_bf16 : 0), a.Hkv, a.B);
   if (D == 128) {
-    if (a.dual)
-      hipLaunchKernelGGL((decode_scan_kernel<128, true>), grid, dim3(kDecThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_scan_kernel<128, false>), grid, dim3(kDecThreads), 0, stream, a);
+    if (a.dual) launch_scan<128, true>(a, grid, stream);
+    else launch_scan<128, false>(a, grid, stream);
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.Hq, a.B), dim3(128), 0, stream, a);
   } else {
-    if (a.dual)
-      hipLaunchKernelGGL((decode_scan_kernel<64, true>), grid, dim3(kDecThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_scan_kernel<64, false>), grid, dim3(kDecThreads), 0, stream, a);
+    if (a.dual) launch_scan<64, true>(a, grid, stream);
+    else launch_scan<64, false>(a, grid, stream);
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.Hq, a.B), dim3(64), 0, stream, a);
   }
   return hipGetLastError();

@@ -118,6 +118,10 @@ struct DecodeArgs {
   const uint16_t* v_sel;
   const uint16_t* k_win;
   const uint16_t* v_win;
+  // paged cache: k, v are pools [n_pages][Hkv][page_size][D]
+  int paged;
+  const int32_t* block_table;  // [B][max_pages]
+  int max_pages, page_size, n_pages;
 };
 
 struct SelectArgs {

@@ -291,6 +291,39 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
                               float* out, float* lse, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * mxattn_decode_paged -- mxattn_decode over a paged MXFP4 KV cache
+ * (BitDecoding-FP4, "System-Level Optimization": the cache is split into
+ * fixed-size pages placed anywhere in GPU memory and found through a block
+ * table, at the cost of indirect loads of codes and scale factors).
+ *   k_pool, v_pool  HD layout with batch = number of pages, seq = page_size:
+ *            codes [n_pages][Hkv][page_size][D/2] (any strides, as for
+ *            mxattn_mx_t), one page holding page_size consecutive tokens of
+ *            one sequence for every KV head.
+ *   paging->block_table  device int32 [B][max_pages]: physical page of the
+ *            sequence's logical page j (tokens [j*page_size, (j+1)*page_size)).
+ *            Entries of pages holding tokens below ctx_len must lie in
+ *            [0, n_pages); any other entry reads as zero codes (never stray
+ *            memory), so it must not be reached.
+ *   Capacity per sequence: Tcap = max_pages * page_size (ctx_len is clamped
+ *   to it on the device; workspace from mxattn_decode_workspace_bytes with
+ *   tcap = Tcap).  Every other argument, the dual-residual query and the
+ *   hybrid set included, is as for mxattn_decode, and the result is the one
+ *   mxattn_decode gives on the contiguous cache the pages spell out.
+ * Supported: page_size a multiple of 32; split_len a multiple of page_size
+ * and at most 64 pages; one page of one head below 2 GiB. */
+typedef struct {
+  const int32_t* block_table;
+  int32_t max_pages;
+} mxattn_paging_t;
+
+mxattn_status_t mxattn_decode_paged(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,
+                                    const mxattn_mx_t* k_pool, const mxattn_mx_t* v_pool,
+                                    const mxattn_paging_t* paging, const int32_t* ctx_len,
+                                    const mxattn_hybrid_t* hybrid, float softmax_scale, int32_t split_len,
+                                    void* workspace, size_t workspace_bytes, float* out, float* lse,
+                                    mxattn_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * mxattn_select_vertical -- accumulate column mass and pick the top-rho
  * vertical-line tokens of the non-window prefix (HyQuant, method paragraphs).
  *   q_recent HD layout [B][Hq][R][D], R <= 64 recent MXFP4 queries.

@@ -239,6 +239,49 @@ def test_decode_workspace_and_rejects():
     assert b"q_res" in lib.mxattn_last_error()
 
 
+@pytest.mark.parametrize("case, status", [
+    ("null_paging", mxa.ERR_INVALID_ARG),
+    ("null_table", mxa.ERR_INVALID_ARG),
+    ("no_pages", mxa.ERR_INVALID_ARG),
+    ("page_48", mxa.ERR_UNSUPPORTED),
+    ("split_not_pages", mxa.ERR_UNSUPPORTED),
+    ("split_65_pages", mxa.ERR_UNSUPPORTED),
+    ("pools_differ", mxa.ERR_INVALID_ARG),
+    ("capacity_overflow", mxa.ERR_UNSUPPORTED),
+    ("workspace_small", mxa.ERR_WORKSPACE),
+])
+def test_decode_paged_rejects(case, status):
+    """Argument checks of mxattn_decode_paged, all taken before any launch."""
+    lib = mxa.library()
+    q = _mx(s=1, h=32, b=4)
+    kp, vp = _mx(b=100, h=8, s=64), _mx(b=100, h=8, s=64)
+    pg = mxa._Paging(8192, 512)  # 512 pages of 64 tokens per sequence
+    split = 2048
+    ws = 1 << 30
+    if case == "page_48":
+        kp, vp = _mx(b=100, h=8, s=48), _mx(b=100, h=8, s=48)
+    elif case == "null_table":
+        pg.block_table = None
+    elif case == "no_pages":
+        pg.max_pages = 0
+    elif case == "split_not_pages":  # 2112 tokens: a multiple of 64, not of the 128-token page
+        kp, vp = _mx(b=100, h=8, s=128), _mx(b=100, h=8, s=128)
+        split = 2112
+    elif case == "split_65_pages":
+        split = 65 * 64
+    elif case == "pools_differ":
+        vp = _mx(b=99, h=8, s=64)
+    elif case == "capacity_overflow":
+        pg.max_pages = (1 << 31) // 64
+    elif case == "workspace_small":
+        ws = 64
+    st = lib.mxattn_decode_paged(ctypes.byref(q), None, None, ctypes.byref(kp), ctypes.byref(vp),
+                                 None if case == "null_paging" else ctypes.byref(pg), ctypes.c_void_p(64), None,
+                                 0.0, split, ctypes.c_void_p(4096), ws, ctypes.c_void_p(4096), None, None)
+    assert st == status, mxa.library().mxattn_last_error()
+    assert len(mxa.library().mxattn_last_error()) > 0
+
+
 def test_quantize_dual_rejects_without_launch():
     lib = mxa.library()
     strides = (ctypes.c_int64 * 3)(0, 0, 128)

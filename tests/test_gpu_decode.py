@@ -179,6 +179,79 @@ def test_decode_hadamard_rotated_query_and_keys():
     assert err_r < err_p
 
 
+def _page_pool(c, page, ctx, seed, spare=7):
+    """Scatter a contiguous MX cache [B, Hkv, T, D] into a shuffled pool of
+    pages (plus `spare` pages of random bytes that nothing may read).  Pages
+    wholly past a sequence's context get table entry -1."""
+    b, hkv, t, d = c.shape
+    maxp = t // page
+    g = torch.Generator().manual_seed(seed)
+    n_pages = b * maxp + spare
+    perm = torch.randperm(n_pages, generator=g)[:b * maxp].reshape(b, maxp).to(torch.int32)
+    used = (torch.arange(maxp)[None, :] * page) < ctx.cpu()[:, None].long()
+    table = torch.where(used, perm, torch.full_like(perm, -1))
+    if spare > 0:
+        codes = torch.randint(0, 256, (n_pages, hkv, page, d // 2), generator=g, dtype=torch.uint8).to(DEV)
+        scales = torch.randint(0, 256, (n_pages, hkv, page, d // 32), generator=g, dtype=torch.uint8).to(DEV)
+    else:
+        codes = torch.zeros((n_pages, hkv, page, d // 2), dtype=torch.uint8, device=DEV)
+        scales = torch.zeros((n_pages, hkv, page, d // 32), dtype=torch.uint8, device=DEV)
+    src_c = c.codes.reshape(b, hkv, maxp, page, d // 2).permute(0, 2, 1, 3, 4).reshape(b * maxp, hkv, page, d // 2)
+    src_s = c.scales.reshape(b, hkv, maxp, page, d // 32).permute(0, 2, 1, 3, 4).reshape(b * maxp, hkv, page, d // 32)
+    sel = used.reshape(-1).to(DEV)
+    dst = perm.reshape(-1).long().to(DEV)[sel]
+    codes[dst] = src_c[sel]
+    scales[dst] = src_s[sel]
+    pool = mxa.MX(codes, scales, (n_pages, hkv, page, d), "hd")
+    return pool, table.contiguous().to(DEV)
+
+
+@pytest.mark.parametrize("page, d, hq, hkv, split", [(32, 128, 8, 2, 1024), (64, 64, 4, 4, 512),
+                                                     (256, 128, 16, 2, 2048), (128, 128, 8, 8, 8192)])
+def test_decode_paged_matches_contiguous(page, d, hq, hkv, split):
+    """The paged scan gives the contiguous scan's outputs bit for bit on the
+    cache its pages spell out (shuffled pages, ragged contexts, pages past the
+    context absent from the table), and the oracle's within tolerance."""
+    g = torch.Generator(device=DEV).manual_seed(40 + page)
+    b, tcap = 3, 2048
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([2048, 1000, 33], dtype=torch.int32, device=DEV)
+    kc, vc = _cache(k, v)
+    kp, table = _page_pool(kc, page, ctx, seed=page)
+    vp, _ = _page_pool(vc, page, ctx, seed=page)
+    qh = _query(q)
+    print(f"paged decode page={page} d={d} hq={hq} hkv={hkv} split={split}", flush=True)
+    ref_o, ref_l = mxa.decode(qh, kc, vc, ctx, split_len=split, return_lse=True)
+    got_o, got_l = mxa.decode_paged(qh, kp, vp, table, ctx, split_len=split, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_o, got_o) and torch.equal(ref_l, got_l)
+    pairs = [(0, 0), (1, hq - 1), (2, hq // 2)]
+    _compare(got_o, got_l, _oracle_pair(q, k, v, ctx, pairs), f"paged page={page}")
+
+
+def test_decode_paged_hybrid_and_dual_query():
+    """A hybrid set and a dual-residual query over the paged cache: the same
+    bits as over the contiguous cache."""
+    g = torch.Generator(device=DEV).manual_seed(45)
+    b, hq, hkv, tcap, d, page = 2, 8, 2, 4096, 128, 64
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([4096, 2500], dtype=torch.int32, device=DEV)
+    kc, vc = _cache(k, v)
+    kp, table = _page_pool(kc, page, ctx, seed=3)
+    vp, _ = _page_pool(vc, page, ctx, seed=3)
+    hy, _ = _hybrid_inputs(q, k, v, ctx, 64, 50, 64, seed=9)
+    q1, q2 = mxa.quantize_dual(q[:, :, None, :])
+    print("paged decode with hybrid set and dual query", flush=True)
+    ref = mxa.decode(q1, kc, vc, ctx, split_len=2048, hybrid=hy, q_bf16=q.contiguous(), q_res=q2)
+    got = mxa.decode_paged(q1, kp, vp, table, ctx, split_len=2048, hybrid=hy, q_bf16=q.contiguous(), q_res=q2)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
+
+
 def _hybrid_inputs(q, k, v, ctx, window, n_sel, max_sel, seed):
     """Seeded selected sets (ascending, below ctx-window) and the gathered
     bf16 rows the decode reads."""
@@ -259,6 +332,17 @@ def test_decode_32k_batch32_full_size():
         assert_codes_equal(sub, *oc, f"cache b{b} kv{kv}")
     ref = _oracle_pair(d["q"], d["k"], d["v"], d["ctx_len"].cpu().numpy(), pairs)
     _compare(out, lse, ref, "decode 32K batch 32")
+    # The same cache as a shuffled pool of 64-token pages, split 4096.
+    del d["k"], d["v"]
+    ref4 = mxa.decode(qh, kc, vc, d["ctx_len"], split_len=4096)
+    kp, table = _page_pool(kc, 64, d["ctx_len"], seed=11, spare=0)
+    del kc
+    vp, _ = _page_pool(vc, 64, d["ctx_len"], seed=11, spare=0)
+    del vc
+    print("decode 32K batch 32, paged (64-token pages)", flush=True)
+    paged = mxa.decode_paged(qh, kp, vp, table, d["ctx_len"], split_len=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(ref4, paged)
 
 
 def test_hybrid_decode_32k_batch8_full_size():
