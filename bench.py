@@ -36,10 +36,10 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # fetch 7064 KiB x 2.000 + write 65831 KiB x 1.000 per dispatch
-    "prefill_kernel<128,128,true,true>": {"bytes": 81877696, "sources": "e508824ecd3b825b"},
-    # fetch 557398 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch
-    "decode_scan_kernel<128> split 4096": {"bytes": 1146006976, "sources": "dbb9d526b2e62268"},
+    # fetch 7050 KiB x 2.000 + write 65814 KiB x 1.000 per dispatch (medians)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81832768, "sources": "ae77f6f4e779ec3c"},
+    # fetch 557404 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch (medians)
+    "decode_scan_kernel<128> split 4096": {"bytes": 1146019264, "sources": "e94b37f0adbe6ee7"},
 }
 TRAFFIC_SOURCES = {
     "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
