@@ -145,6 +145,27 @@ def test_prefill_hybrid_rejects(case, status):
     assert len(mxa.library().mxattn_last_error()) > 0
 
 
+@pytest.mark.parametrize("shape, status", [
+    ((0, 1, 128, 128), mxa.ERR_INVALID_ARG), ((1, 0, 128, 128), mxa.ERR_INVALID_ARG),
+    ((1, 1, 0, 128), mxa.ERR_INVALID_ARG), ((65536, 1, 32, 128), mxa.ERR_UNSUPPORTED),
+    ((1, 65536, 32, 128), mxa.ERR_UNSUPPORTED), ((1, 1, (1 << 26) + 32, 64), mxa.ERR_UNSUPPORTED),
+    ((1, 1, 128, 256), mxa.ERR_UNSUPPORTED),
+])
+def test_empty_and_oversized_shapes_rejected(shape, status):
+    """Empty tensors and shapes past the grid limits are refused by every
+    entry point before any launch."""
+    lib = mxa.library()
+    b, h, s, d = shape
+    q, k, v = _mx(b=b, h=h, s=s, d=d), _mx(b=b, h=h, s=s, d=d), _mx(b=b, h=h, s=s, d=d, layout=1)
+    assert _prefill(q, k, v) == status
+    strides = (ctypes.c_int64 * 3)(h * s * d, s * d, d)
+    assert lib.mxattn_quantize(ctypes.c_void_p(4096), 2, strides, None, 0, 7.25, 0, ctypes.byref(q), None) == status
+    q1 = _mx(b=b, h=h, s=1, d=d) if s != 0 else _mx(b=b, h=h, s=0, d=d)
+    st = lib.mxattn_decode(ctypes.byref(q1), None, None, ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(64), None,
+                           0.0, 2048, ctypes.c_void_p(4096), 1 << 40, ctypes.c_void_p(4096), None, None)
+    assert st == status, lib.mxattn_last_error()
+
+
 def test_quantize_rejects_without_launch():
     lib = mxa.library()
     out = _mx()

@@ -427,3 +427,23 @@ def test_select_vertical_32k_batch8():
         top = np.sort(ocm[:32640])[::-1]
         frac = top[:1632].sum() / top.sum()
         print(f"  b{b} h{h}: top-5% non-window mass fraction {frac:.3f}", flush=True)
+
+
+def test_decode_degenerate_zero_query_gives_mean():
+    """q = 0: all logits 0, so the output is the mean of the first ctx
+    dequantised V rows (closed form) and lse = ln(ctx)."""
+    g = torch.Generator(device=DEV).manual_seed(83)
+    b, hq, hkv, tcap, d = 2, 4, 2, 1000, 128
+    q = torch.zeros((b, hq, d), device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([1000, 77], dtype=torch.int32, device=DEV)
+    kc, vc = _cache(k, v)
+    out, lse = mxa.decode(_query(q), kc, vc, ctx, split_len=256, return_lse=True)
+    torch.cuda.synchronize()
+    vd = oracle_dequant(*oracle_quantize(host_f64(v), "hd"), "hd")
+    for bb in range(b):
+        c = int(ctx[bb])
+        for h in range(hq):
+            np.testing.assert_allclose(out[bb, h].cpu().numpy(), vd[bb, h // 2, :c].mean(axis=0), atol=1e-5, rtol=0)
+            assert abs(float(lse[bb, h]) - np.log(c)) < 1e-5

@@ -330,3 +330,42 @@ def test_hybrid_prefill_cuts_error_on_heavy_columns():
         e_h.append(np.abs(hyb[0, h] - ref).mean())
     print(f"  mean |out - exact|: 4-bit {np.mean(e_p):.3e}, hybrid {np.mean(e_h):.3e}", flush=True)
     assert np.mean(e_h) < 0.8 * np.mean(e_p)
+
+
+def test_degenerate_zero_query_gives_running_mean():
+    """All logits 0: every P~ is 1, so P_hat = 1 exactly and the causal output
+    of row i is the mean of the dequantised V rows 0..i (closed form, no
+    attention code involved); lse = ln(i + 1)."""
+    g = torch.Generator(device=DEV).manual_seed(81)
+    s, d = 300, 128
+    q = torch.zeros((1, 2, s, d), device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((1, 1, s, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, 1, s, d), generator=g, device=DEV).to(torch.bfloat16)
+    qh, kh, vh = mxa.quantize(q), mxa.quantize(k), mxa.quantize(v, "key")
+    for tile in (64, 128, 256):
+        out, lse = mxa.prefill(qh, kh, vh, causal=True, kv_tile=tile, return_lse=True)
+        torch.cuda.synchronize()
+        vd = oracle_dequant(*oracle_quantize(host_f64(v), "key"), "key", n=s)[0, 0]
+        mean = np.cumsum(vd, axis=0) / np.arange(1, s + 1)[:, None]
+        for h in range(2):
+            np.testing.assert_allclose(out[0, h].cpu().numpy(), mean, atol=1e-5, rtol=0)
+            np.testing.assert_allclose(lse[0, h].cpu().numpy(), np.log(np.arange(1, s + 1)), atol=1e-5, rtol=0)
+
+
+def test_degenerate_one_dominant_key_gives_its_row():
+    """One key whose logit beats every other by far more than the fp32
+    exponent range: the softmax is one-hot, so each row from that key on
+    outputs that key's dequantised V row exactly."""
+    g = torch.Generator(device=DEV).manual_seed(82)
+    s, d, hot = 256, 128, 37
+    q = torch.randn((1, 1, s, d), generator=g, device=DEV).abs().to(torch.bfloat16)
+    k = (torch.randn((1, 1, s, d), generator=g, device=DEV) * 0.01).to(torch.bfloat16)
+    k[0, 0, hot] = 400.0
+    v = torch.randn((1, 1, s, d), generator=g, device=DEV).to(torch.bfloat16)
+    qh, kh, vh = mxa.quantize(q), mxa.quantize(k), mxa.quantize(v, "key")
+    out = mxa.prefill(qh, kh, vh, causal=True)
+    torch.cuda.synchronize()
+    vd = oracle_dequant(*oracle_quantize(host_f64(v), "key"), "key", n=s)[0, 0]
+    o = out[0, 0].cpu().numpy()
+    np.testing.assert_array_equal(o[hot:], np.broadcast_to(vd[hot], (s - hot, d)).astype(np.float32))
+    _run_case(q, k, v, causal=True, what="one dominant key")
