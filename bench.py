@@ -8,7 +8,9 @@ outlier K channels, static Smooth-QK): MXFP4 quantisation of Q, K, V plus the
 attention kernel.  `value` is algorithmic TFLOP/s of that step (4*D flops per
 unmasked query-key pair, the two contractions only).  The 32K decode legs
 (plain and hybrid) are reported in the same line under "decode" and
-"hybrid_decode" with ms/token, GB/s and their HBM roofline.
+"hybrid_decode" with ms/token, GB/s and their HBM roofline; the 32K
+non-causal prefill with UOS scales (24 heads, 13.2 TFLOP per call) under
+"diffusion_prefill" with its MXFP4 roofline.
 
 Inputs are generated on the GPU from fixed seeds (synth); they are resident in
 HBM before any timed region.  Calibration of the Smooth-QK factors is offline
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,hybrid",
+    ap.add_argument("--legs", default="prefill,diffusion,decode,hybrid",
                     help="comma list of legs to run (prefill is the headline)")
     ap.add_argument("--kv-tile", type=int, default=128)
     ap.add_argument("--decode-split", type=int, default=4096, help="tokens per split, 32K decode leg")
@@ -85,7 +87,10 @@ def parse():
 
 def timed(fn, steps, warmup, kernel_fn=None):
     """Wall time per step over `steps` steps after `warmup` untimed ones, and
-    the mean duration of kernel_fn measured with events on the current stream."""
+    the mean duration of kernel_fn: `steps` back-to-back launches bracketed
+    by two events on the launch stream (the library launches on torch's
+    current stream), total / steps.  Per-launch event pairs would add the
+    host's call time whenever the queue runs dry."""
     import torch
     for _ in range(warmup):
         fn()
@@ -97,13 +102,14 @@ def timed(fn, steps, warmup, kernel_fn=None):
     wall = (time.perf_counter() - t0) / steps
     kern = None
     if kernel_fn is not None:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in evs:
-            a.record()
+        kernel_fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
             kernel_fn()
-            b.record()
+        b.record()
         torch.cuda.synchronize()
-        kern = sum(a.elapsed_time(b) for a, b in evs) / steps / 1e3
+        kern = a.elapsed_time(b) / steps / 1e3
     return wall, kern
 
 
@@ -418,6 +424,50 @@ def hybrid_leg(args, flush):
     }
 
 
+# ------------------------------------------------------------------ long non-causal
+def diffusion_leg(args):
+    """Non-causal video-diffusion-style prefill: batch 1, 24 heads, seq 32768
+    (8 x 64 x 64 token grid), head_dim 128, low-rank spatially correlated
+    bf16 Q/K/V; UOS (Qmax 7.25) scales on Q, K, V and P; P-Reordering/PNQ."""
+    import torch
+    import bit_microscaled_flashattention_amd as mxa
+    import synth
+
+    B, H, S, D = 1, 24, 32768, 128
+    d = synth.diffusion(device="cuda")
+    qh = mxa.empty_mx((B, H, S, D), "hd")
+    kh = mxa.empty_mx((B, H, S, D), "hd")
+    vh = mxa.empty_mx((B, H, S, D), "key")
+    out = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
+    jobs = [dict(x=d["q"], rule="uos", out=qh), dict(x=d["k"], rule="uos", out=kh),
+            dict(x=d["v"], layout="key", rule="uos", out=vh)]
+
+    def attn():
+        mxa.prefill(qh, kh, vh, causal=False, kv_tile=args.kv_tile, p_rule="uos", out=out)
+
+    def step():
+        mxa.quantize_batch(jobs)
+        attn()
+
+    steps, warm = max(args.steps // 4, 3), max(args.warmup // 2, 1)
+    wall, kern = timed(step, steps, warm, attn)
+    flops = 4 * D * B * H * S * S
+    del d, out
+    torch.cuda.empty_cache()
+    return {
+        "workload": "non-causal video-diffusion attention: batch 1, 24 heads, seq 32768 (8x64x64 grid), head_dim "
+                    "128, bf16 Q/K/V with 16 low-frequency Fourier modes (lambda 0.5), UOS Qmax 7.25 on Q, K, V "
+                    f"and P, PNQ, kv_tile {args.kv_tile}; step = quantise Q,K,V + attention",
+        "ms_per_step": round(wall * 1e3, 4),
+        "step_tflops": round(flops / wall / 1e12, 2),
+        "flops": flops,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,128,non-causal,uos>",
+                     "achieved": round(flops / kern / 1e12, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / kern / 1e12 / PEAK_FP4_TFLOPS, 4),
+                     "kernel_ms": round(kern * 1e3, 4), "traffic": None},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -464,6 +514,8 @@ def main():
     }
     del d
     torch.cuda.empty_cache()
+    if "diffusion" in legs:
+        line["diffusion_prefill"] = diffusion_leg(args)
     if legs & {"decode", "hybrid"}:
         flush = _flush_buffer()
         if "decode" in legs:

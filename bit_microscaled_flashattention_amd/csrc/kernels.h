@@ -39,10 +39,14 @@ constexpr int kMaxSlots = 4096;
 // workgroup of job i and start[n] the grid size, gx[i] the workgroups along
 // the sequence of one (batch, head) of job i.
 constexpr int kMaxQuantJobs = 4;
+// flat[i]: job i has fewer head-dim blocks per (batch, head) than one
+// workgroup covers (a decode query, S = 1), so its workgroups run over the
+// rows of all heads and batches in order instead of one head each.
 struct QuantBatch {
   QuantArgs job[kMaxQuantJobs];
   int start[kMaxQuantJobs + 1];
   int gx[kMaxQuantJobs];
+  int flat[kMaxQuantJobs];
   int n;
 };
 

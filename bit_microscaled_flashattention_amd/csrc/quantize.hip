@@ -85,21 +85,38 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 }
 
 template <int DT>
-__device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h, int64_t b) {
+__device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h, int64_t b, bool flat) {
   const int nblk_row = static_cast<int>(a.D) / 32;   // 2 or 4
-  const int total = static_cast<int>(a.S) * nblk_row;
+  // Blocks this launch covers for the workgroup's range: those of one head,
+  // or (flat) those of every row of the tensor in (batch, head, row) order.
+  const int64_t total = flat ? a.B * a.H * a.S * nblk_row : a.S * nblk_row;
   const int lane = threadIdx.x & 63;
   const int wave = x * 4 + (threadIdx.x >> 6);
   const int part = lane & 3;
-  const int64_t head_off = b * a.xs[0] + h * a.xs[1];
 
+  // Per group r: its block, and the (batch, head, row) that block lies in.
+  int64_t blk[kHdRows], hr[kHdRows], br[kHdRows], sr[kHdRows];
+#pragma unroll
+  for (int r = 0; r < kHdRows; ++r) {
+    blk[r] = (static_cast<int64_t>(wave) * kHdRows + r) * 16 + (lane >> 2);
+    const int64_t row = blk[r] / nblk_row;
+    if (flat) {
+      sr[r] = row % a.S;
+      const int64_t bh = row / a.S;
+      hr[r] = bh % a.H;
+      br[r] = bh / a.H;
+    } else {
+      sr[r] = row;
+      hr[r] = h;
+      br[r] = b;
+    }
+  }
   float y[kHdRows][8];
 #pragma unroll
   for (int r = 0; r < kHdRows; ++r) {
-    const int blk = (wave * kHdRows + r) * 16 + (lane >> 2);
-    if (blk < total) {
-      const int64_t s = blk / nblk_row;
-      load8<DT>(a.x, head_off + s * a.xs[2] + ((blk & (nblk_row - 1)) * 32 + part * 8), y[r]);
+    if (blk[r] < total) {
+      load8<DT>(a.x, br[r] * a.xs[0] + hr[r] * a.xs[1] + sr[r] * a.xs[2] + ((blk[r] & (nblk_row - 1)) * 32 + part * 8),
+                y[r]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[r][k] = 0.0f;
@@ -110,15 +127,18 @@ __device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h
   const int db = (lane >> 2) & (nblk_row - 1);
   const int d0 = db * 32 + part * 8;
   if (a.chan_scale != nullptr) {
-    const v4f c0 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0);
-    const v4f c1 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0 + 4);
 #pragma unroll
-    for (int r = 0; r < kHdRows; ++r)
+    for (int r = 0; r < kHdRows; ++r) {
+      // One head per workgroup: both groups share the factors.
+      const int64_t hh = (flat || r == 0) ? (blk[r] < total ? hr[r] : 0) : hr[0];
+      const v4f c0 = *reinterpret_cast<const v4f*>(a.chan_scale + hh * a.D + d0);
+      const v4f c1 = *reinterpret_cast<const v4f*>(a.chan_scale + hh * a.D + d0 + 4);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         y[r][k] = __fmul_rn(y[r][k], c0[k]);
         y[r][4 + k] = __fmul_rn(y[r][4 + k], c1[k]);
       }
+    }
   }
   if (a.hadamard) {
     // Normalised Walsh-Hadamard transform of each row (BitDecoding-FP4,
@@ -153,8 +173,6 @@ __device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h
   }
 #pragma unroll
   for (int r = 0; r < kHdRows; ++r) {
-    const int blk = (wave * kHdRows + r) * 16 + (lane >> 2);
-    const int64_t s = blk / nblk_row;
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -182,14 +200,15 @@ __device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h
       sb2 = e8m0_byte(amax2, a.uos, a.qmax_quarter);
       packed2 = encode8(res, sb2);
     }
-    if (blk >= total) continue;
-    uint8_t* crow = a.codes + b * a.cs[0] + h * a.cs[1] + s * a.cs[2];
+    if (blk[r] >= total) continue;
+    const int64_t bb = br[r], hh = hr[r], s = sr[r];
+    uint8_t* crow = a.codes + bb * a.cs[0] + hh * a.cs[1] + s * a.cs[2];
     *reinterpret_cast<uint32_t*>(crow + d0 / 2) = packed;
-    if (part == 0) a.scales[b * a.ss[0] + h * a.ss[1] + s * a.ss[2] + db] = static_cast<uint8_t>(sb);
+    if (part == 0) a.scales[bb * a.ss[0] + hh * a.ss[1] + s * a.ss[2] + db] = static_cast<uint8_t>(sb);
     if (a.codes2 != nullptr) {
-      uint8_t* crow2 = a.codes2 + b * a.cs2[0] + h * a.cs2[1] + s * a.cs2[2];
+      uint8_t* crow2 = a.codes2 + bb * a.cs2[0] + hh * a.cs2[1] + s * a.cs2[2];
       *reinterpret_cast<uint32_t*>(crow2 + d0 / 2) = packed2;
-      if (part == 0) a.scales2[b * a.ss2[0] + h * a.ss2[1] + s * a.ss2[2] + db] = static_cast<uint8_t>(sb2);
+      if (part == 0) a.scales2[bb * a.ss2[0] + hh * a.ss2[1] + s * a.ss2[2] + db] = static_cast<uint8_t>(sb2);
     }
   }
 }
@@ -272,6 +291,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch p) {
   for (int i = 1; i < kMaxQuantJobs; ++i) j += (i < p.n && bid >= p.start[i]) ? 1 : 0;
   const QuantArgs& a = p.job[j];
   const int local = bid - p.start[j];
+  if (p.flat[j]) {
+    if (a.dtype == 2) quantize_hd<2>(a, local, 0, 0, true);
+    else if (a.dtype == 1) quantize_hd<1>(a, local, 0, 0, true);
+    else quantize_hd<0>(a, local, 0, 0, true);
+    return;
+  }
   const int gx = p.gx[j];
   const int x = local % gx;
   const int rest = local / gx;
@@ -282,9 +307,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch p) {
     else if (a.dtype == 1) quantize_key<1>(a, x, h, b, tile);
     else quantize_key<0>(a, x, h, b, tile);
   } else {
-    if (a.dtype == 2) quantize_hd<2>(a, x, h, b);
-    else if (a.dtype == 1) quantize_hd<1>(a, x, h, b);
-    else quantize_hd<0>(a, x, h, b);
+    if (a.dtype == 2) quantize_hd<2>(a, x, h, b, false);
+    else if (a.dtype == 1) quantize_hd<1>(a, x, h, b, false);
+    else quantize_hd<0>(a, x, h, b, false);
   }
 }
 
@@ -338,12 +363,17 @@ hipError_t launch_quantize_batch(const QuantArgs* jobs, int n, hipStream_t strea
     for (int i = 0; i < n; ++i) {
       const QuantArgs& a = jobs[i];
       if ((a.key_layout != 0) != (pass == 0)) continue;
+      const int64_t blocks_head = a.S * (a.D / 32);
+      const bool flat = !a.key_layout && blocks_head < kHdBlocksPerGroup;
       const int64_t gx = a.key_layout ? (a.S + kKeyChunk - 1) / kKeyChunk
-                                      : (a.S * (a.D / 32) + kHdBlocksPerGroup - 1) / kHdBlocksPerGroup;
+                                      : (blocks_head + kHdBlocksPerGroup - 1) / kHdBlocksPerGroup;
+      const int64_t n_wg = flat ? (blocks_head * a.H * a.B + kHdBlocksPerGroup - 1) / kHdBlocksPerGroup
+                                : gx * a.H * a.B;
       p.job[k] = a;
       p.gx[k] = static_cast<int>(gx);
+      p.flat[k] = flat ? 1 : 0;
       p.start[k] = static_cast<int>(total);
-      total += gx * a.H * a.B;
+      total += n_wg;
       if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
       ++k;
     }

@@ -109,6 +109,32 @@ def test_workload_shapes_q_k_v():
         assert_codes_equal(got, oc, os_, f"4K GQA prefill {name}")
 
 
+@pytest.mark.parametrize("shape", [(32, 32, 1, 128), (3, 5, 3, 128), (2, 7, 9, 64), (1, 1, 1, 64)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_few_rows_per_head(shape, dtype):
+    """Tensors with fewer head-dim blocks per (batch, head) than one
+    workgroup covers (a decode query) run over the rows of every head in one
+    range: codes and scales bit-exact, with per-head channel factors, the
+    Hadamard rotation, and both halves of the dual-residual query."""
+    g = torch.Generator().manual_seed(47)
+    b, h, s, d = shape
+    x = (torch.randn(shape, generator=g) * 2).to(dtype)
+    cs = torch.exp(torch.randn((h, d), generator=g)).to(torch.float32)
+    print(f"quantize few rows {shape} {dtype}", flush=True)
+    x32 = smooth.apply(host_f64(x).astype(np.float32), cs.numpy())
+    got = mxa.quantize(x.to(DEV), layout="hd", chan_scale=cs.to(DEV))
+    rot = mxa.quantize(x.to(DEV), layout="hd", chan_scale=cs.to(DEV), hadamard=True)
+    q1, q2 = mxa.quantize_dual(x.to(DEV), chan_scale=cs.to(DEV), rule="uos")
+    torch.cuda.synchronize()
+    oc, os_ = oracle_quantize(x32.astype(np.float64), "hd")
+    assert_codes_equal(got, oc, os_, f"few rows {shape}")
+    rc, rs = oracle_quantize(rotate.hadamard_f32(x32, axis=3).astype(np.float64), "hd")
+    assert_codes_equal(rot, rc, rs, f"few rows rotated {shape}")
+    c1, s1, c2, s2 = mx.quantize_dual(x32.astype(np.float64), axis=3, rule=mx.RULE_UOS)
+    assert_codes_equal(q1, c1, s1, f"few rows dual first half {shape}")
+    assert_codes_equal(q2, c2, s2, f"few rows dual residual {shape}")
+
+
 @pytest.mark.parametrize("rule", ["ocp", "uos"])
 def test_quantize_dual_bit_exact(rule):
     """Both halves of the dual-residual query, codes and scale bytes, bit for
