@@ -78,7 +78,9 @@ def parse():
                     help="comma list of legs to run (prefill is the headline)")
     ap.add_argument("--kv-tile", type=int, default=128)
     ap.add_argument("--decode-split", type=int, default=4096, help="tokens per split, 32K decode leg")
-    ap.add_argument("--hybrid-split", type=int, default=2048, help="tokens per split, hybrid decode leg")
+    ap.add_argument("--hybrid-split", type=int, default=2752,
+                    help="tokens per split, hybrid decode leg (12 splits x 64 (sequence, KV head) = 768 workgroups: "
+                         "one round at three per CU)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run an elementwise kernel of known size (1 GiB in, 1 GiB out) three times, "
                          "to scale HBM byte counters; prints the source digests of the profiled kernels")

@@ -421,6 +421,8 @@ static mxattn_status_t decode_common(const mxattn_mx_t* q, const mxattn_mx_t* q_
   const int64_t n_split = (tcap + split_len - 1) / split_len;
   if (n_split + bf16_slots(hybrid_rows) > kMaxSlots)
     return fail(MXATTN_ERR_UNSUPPORTED, "decode: more than %lld partial slots; use a longer split_len", (long long)kMaxSlots);
+  if ((n_split + bf16_slots(hybrid_rows)) * q->batch * kc->heads > 0x7FFFFFFF)
+    return fail(MXATTN_ERR_UNSUPPORTED, "decode: problem too large for one launch");
   const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, tcap, split_len,
                                                     static_cast<int32_t>(hybrid_rows));
   if (workspace == nullptr || workspace_bytes < need)

@@ -517,16 +517,24 @@ __device__ __forceinline__ void bf16_part(const DecodeArgs& a, uint8_t* vstage, 
   combine_store<D>(vstage, st, a, b, hk, a.n_split + part_id, a.n_split + a.n_bf16);
 }
 
-// One launch for the whole scan: blockIdx.x < n_split are the 4-bit splits,
-// the rest the bf16 hybrid parts, so the two kinds share the machine.
+// One launch for the whole scan, longest work first: the first
+// n_split x Hkv x B workgroups are the 4-bit splits (split fastest), the
+// rest the shorter bf16 hybrid parts, which fill the slots the splits free
+// at the end.
 template <int D, bool DUAL, bool PAGED>
 __global__ __launch_bounds__(kDecThreads, 3) void decode_scan_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vstage[kStageBytes];
   __shared__ uint32_t selbits[kMaxSplitWords];
-  if (static_cast<int>(blockIdx.x) < a.n_split)
-    fp4_split<D, DUAL, PAGED>(a, vstage, selbits, blockIdx.x, blockIdx.y, blockIdx.z);
-  else
-    bf16_part<D>(a, vstage, blockIdx.x - a.n_split, blockIdx.y, blockIdx.z);
+  const int bid = static_cast<int>(blockIdx.x);
+  const int n4 = a.n_split * a.Hkv * a.B;
+  if (bid < n4) {
+    const int bh = bid / a.n_split;
+    fp4_split<D, DUAL, PAGED>(a, vstage, selbits, bid % a.n_split, bh % a.Hkv, bh / a.Hkv);
+  } else {
+    const int r = bid - n4;
+    const int bh = r / a.n_bf16;
+    bf16_part<D>(a, vstage, r % a.n_bf16, bh % a.Hkv, bh / a.Hkv);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -587,7 +595,7 @@ static void launch_scan(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {
-  const dim3 grid(a.n_split + (a.hybrid ? a.n_bf16 : 0), a.Hkv, a.B);
+  const dim3 grid((a.n_split + (a.hybrid ? a.n_bf16 : 0)) * a.Hkv * a.B);
   if (D == 128) {
     if (a.dual) launch_scan<128, true>(a, grid, stream);
     else launch_scan<128, false>(a, grid, stream);

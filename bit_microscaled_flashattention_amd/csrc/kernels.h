@@ -32,7 +32,7 @@ struct QuantArgs {
 
 // bf16 hybrid rows per decode workgroup (one partial slot each), and the
 // partial slots per (sequence, query head) the decode merge accepts.
-constexpr int kBf16Rows = 256;
+constexpr int kBf16Rows = 512;
 constexpr int kMaxSlots = 4096;
 
 // Up to kMaxQuantJobs tensors quantised by one launch; start[i] is the first

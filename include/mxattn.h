@@ -259,7 +259,7 @@ mxattn_status_t mxattn_prefill_hybrid(const mxattn_mx_t* q, const mxattn_mx_t* k
  *            every other token uses the MXFP4 operands.  Each token counts
  *            once; one softmax covers all of them.
  *   split_len  tokens per split (multiple of 64; at most 8192 with a hybrid
- *            set); the splits (and the bf16 set, in parts of 256 rows) are
+ *            set); the splits (and the bf16 set, in parts of 512 rows) are
  *            merged with their log-sum-exp in a fixed order (deterministic);
  *            at most 4096 parts in total.
  *   workspace  device memory of mxattn_decode_workspace_bytes(...) bytes.
