@@ -228,7 +228,7 @@ def test_decode_workspace_and_rejects():
     n = mxa.decode_workspace_bytes(32, 32, 8, 128, 32768, 2048)
     assert n == 32 * 32 * 16 * 130 * 4
     nh = mxa.decode_workspace_bytes(8, 32, 8, 128, 32768, 2048, hybrid_rows=1632 + 128)
-    assert nh == 8 * 32 * (16 + 7) * 130 * 4
+    assert nh == 8 * 32 * (16 + 4) * 130 * 4      # bf16 set in parts of 512 rows
     assert mxa.decode_workspace_bytes(0, 32, 8, 128, 32768, 2048) == 0
     q = _mx(s=1, h=32); kc = _mx(s=32768, h=8); vc = _mx(s=32768, h=8)
     ctx = ctypes.c_void_p(64)
@@ -348,3 +348,43 @@ def test_python_errors_raise():
     with pytest.raises(mxa.MxattnError) as ei:
         mxa._check(mxa.ERR_UNSUPPORTED)
     assert ei.value.status == mxa.ERR_UNSUPPORTED
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "mxattn.h"
+int main(void) {
+  const mxattn_prefill_params_t p = {1, 0.0f, 128, MXATTN_SCALE_OCP, 7.25f, 1};
+  int64_t shape[4] = {1, 1, 32, 128};
+  mxattn_mx_t m = {0};
+  /* Refused on the host before any launch: null codes. */
+  const mxattn_status_t st = mxattn_prefill(&m, &m, &m, &p, 0, MXATTN_F32, 0, 0);
+  (void)shape;
+  printf("%d|%s|%s|%zu\n", (int)st, mxattn_status_string(st), mxattn_version(),
+         mxattn_decode_workspace_bytes(32, 32, 8, 128, 32768, 4096, 0));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/mxattn.h compiles as strict C99 and a C program links against
+    the library and calls it (host-side entry points only)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(mxa.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                        os.path.dirname(HEADER), str(src), "-o", str(exe), "-L", libdir, "-l:libmxattn.so",
+                        f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    st, text, version, ws = out.stdout.strip().split("|")
+    assert int(st) == 1 and "invalid" in text and "gfx950" in version
+    assert int(ws) == mxa.decode_workspace_bytes(32, 32, 8, 128, 32768, 4096)
