@@ -10,6 +10,7 @@
 //                               callers' error handling).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -259,6 +260,21 @@ mxattn_status_t mxattn_smooth_calibrate(const void* q_cal, const void* k_cal, mx
   return after_launch(launch_smooth_calibrate(a, s), s, "smooth_calibrate");
 }
 
+// Compute units of the current device, read once per device (0 if unknown).
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 static mxattn_status_t prefill_common(const mxattn_mx_t* q, const mxattn_mx_t* k, const mxattn_mx_t* v,
                                       const mxattn_prefill_params_t* p, const mxattn_prefill_hybrid_t* hy,
                                       void* out, mxattn_dtype_t out_dtype, float* lse, mxattn_stream_t stream) {
@@ -328,6 +344,17 @@ static mxattn_status_t prefill_common(const mxattn_mx_t* q, const mxattn_mx_t* k
     a.sel_n = hy->n_sel;
     a.max_sel = hy->max_sel;
     a.window = hy->window;
+  }
+  // Paired schedule: a causal 4-bit launch whose query blocks, two per
+  // workgroup, make exactly one round of two workgroups per CU (kv_tile 256
+  // holds one workgroup per CU), with whole KV heads per XCD.
+  if (hy == nullptr && p->causal && kv_tile != 256 && a.n_qblk >= 4 && a.n_qblk % 4 == 0 &&
+      (a.B * a.Hkv) % 8 == 0) {
+    const int n_cu = device_cu_count();
+    if (n_cu > 0 && static_cast<int64_t>(a.n_qblk) * a.B * a.Hq == 4LL * n_cu) {
+      a.paired = 1;
+      a.pair_c = (27 * (a.n_qblk + 1) + 50) / 100;   // heavy pairs hold about 1.27x the mean tiles
+    }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return after_launch(launch_prefill(a, static_cast<int>(q->dim), kv_tile, p->causal != 0, s), s,

@@ -92,6 +92,11 @@ struct PrefillArgs {
   const int32_t* sel_n;    // [B][Hkv]
   int max_sel;
   int window;
+  // Paired causal schedule: two query blocks per workgroup, heavier pairs
+  // first (see map_pair); pair_c is the first block of the heavy pairs'
+  // short halves.
+  int paired;
+  int pair_c;
 };
 
 // Longest sequence of the hybrid prefill: the selected-key bitmap of a

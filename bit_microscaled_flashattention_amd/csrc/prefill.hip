@@ -285,21 +285,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
 }
 
+// Paired causal schedule (a.paired): one round of workgroups, each running
+// two query blocks of one query head in turn.  On this GPU the workgroups
+// of a CU are issued oldest first: the one dispatched first (the lower
+// half of the grid when the grid fills every CU twice) runs about 1.8x
+// faster than its neighbour.  So the first half takes pairs of about 1.27x
+// the mean tiles and the second half the rest, and the two on a CU finish
+// together instead of one running alone at the end.  With N query blocks
+// per head (N % 4 == 0) and c = a.pair_c, the heavy pairs are
+// (N-1-i, c+i), i < N/4; the light pairs take the remaining blocks
+// smallest with largest.  Each XCD (bid % 8) works on whole KV heads, as in
+// map_block.  qb2 = -1: no second block.
+__device__ __forceinline__ void map_pair(const PrefillArgs& a, int& qb1, int& qb2, int& b, int& hq) {
+  const int G = a.Hq / a.Hkv;
+  const int N = a.n_qblk, N4 = N / 4;
+  const int per = (a.B * a.Hkv) / 8;          // (batch, KV head) pairs per XCD
+  const int slot = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int heavy = per * G * N4;             // heavy workgroups per XCD
+  const bool is_heavy = local < heavy;
+  const int l2 = is_heavy ? local : local - heavy;
+  const int head = l2 / N4, m = l2 % N4;      // query head of the XCD's range, pair index
+  const int pair = slot * per + head / G;
+  b = pair / a.Hkv;
+  hq = (pair % a.Hkv) * G + head % G;
+  if (is_heavy) {
+    qb1 = N - 1 - m;
+    qb2 = a.pair_c + m;
+  } else {
+    // The remaining blocks {0..c-1} and {c+N/4 .. 3N/4-1}, r-th in order.
+    auto rest = [&](int r) { return r < a.pair_c ? r : r + N4; };
+    qb1 = rest(N / 2 - 1 - m);
+    qb2 = rest(m);
+  }
+}
+
 template <int D, int BC, bool CAUSAL, bool LQ, bool PUOS, bool HYB>
-__global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int qb, const int b, const int hq,
+                                             uint8_t* __restrict__ smem, uint32_t* __restrict__ selmap) {
   using C = Cfg<D, BC>;
-  static_assert(!HYB || CAUSAL, "the hybrid kernel is causal");
-  constexpr int SMEM = (HYB && 2 * HybCfg<D>::BYTES > 2 * C::STAGE) ? 2 * HybCfg<D>::BYTES : 2 * C::STAGE;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  // Padded by 8 words: a tile reads the words of all its blocks at once
-  // (those past the last row belong to empty blocks and are never used).
-  __shared__ __attribute__((aligned(16))) uint32_t selmap[HYB ? kHybSelWords + 8 : 1];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, j = lane & 31, hh = lane >> 5;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-
-  int qb, b, hq;
-  map_block(a, CAUSAL, qb, b, hq);
   const int hk = hq / (a.Hq / a.Hkv);
   const int q0 = qb * kBR;
   const int my_q = q0 + wave_s * 32 + j;
@@ -813,9 +839,31 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
     }
 }
 
+template <int D, int BC, bool CAUSAL, bool LQ, bool PUOS, bool HYB>
+__global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
+  using C = Cfg<D, BC>;
+  static_assert(!HYB || CAUSAL, "the hybrid kernel is causal");
+  constexpr int SMEM = (HYB && 2 * HybCfg<D>::BYTES > 2 * C::STAGE) ? 2 * HybCfg<D>::BYTES : 2 * C::STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  // Padded by 8 words: a tile reads the words of all its blocks at once
+  // (those past the last row belong to empty blocks and are never used).
+  __shared__ __attribute__((aligned(16))) uint32_t selmap[HYB ? kHybSelWords + 8 : 1];
+  int qb1, qb2 = -1, b, hq;
+  if (!HYB && CAUSAL && a.paired) map_pair(a, qb1, qb2, b, hq);
+  else map_block(a, CAUSAL, qb1, b, hq);
+  prefill_item<D, BC, CAUSAL, LQ, PUOS, HYB>(a, qb1, b, hq, smem, selmap);
+  if (qb2 >= 0) {
+    // The first block's last tile step ended with a barrier; this one keeps
+    // its output epilogue clear of the next block's LDS writes as well.
+    __syncthreads();
+    prefill_item<D, BC, CAUSAL, LQ, PUOS, HYB>(a, qb2, b, hq, smem, selmap);
+  }
+}
+
 template <int D, int BC, bool PUOS>
 static void launch_tp(const PrefillArgs& a, int causal, bool hyb, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(a.n_qblk) * a.B * a.Hq;
+  unsigned grid = static_cast<unsigned>(a.n_qblk) * a.B * a.Hq;
+  if (a.paired) grid /= 2;
   const bool lq = a.l_from_quantized != 0;
   if (hyb && lq)
     hipLaunchKernelGGL((prefill_kernel<D, BC, true, true, PUOS, true>), dim3(grid), dim3(kThreads), 0, stream, a);

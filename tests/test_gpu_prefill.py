@@ -174,6 +174,31 @@ def test_diffusion_prefill_sampled_rows():
               heads=heads, what="video diffusion full size")
 
 
+@pytest.mark.parametrize("shape", [(1, 32, 8, 4096), (2, 16, 8, 4096), (1, 64, 8, 2048)])
+def test_causal_schedule_matches_per_head_launches(shape):
+    """Causal launches whose query blocks fill every CU exactly twice over run
+    two blocks per workgroup (heavier pairs first).  Rows are independent, so
+    output and lse equal, bit for bit, separate launches over each KV head's
+    group (which are too small to be paired)."""
+    b, hq, hkv, s = shape
+    g = torch.Generator(device=DEV).manual_seed(27)
+    print(f"paired schedule {shape}", flush=True)
+    q = torch.randn((b, hq, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    qh, kh, vh = mxa.quantize(q, "hd"), mxa.quantize(k, "hd"), mxa.quantize(v, "key")
+    out, lse = mxa.prefill(qh, kh, vh, causal=True, return_lse=True)
+    grp = hq // hkv
+    for bi in range(b):
+        for h in range(hkv):
+            qs = mxa.quantize(q[bi:bi + 1, h * grp:(h + 1) * grp].contiguous(), "hd")
+            ks = mxa.quantize(k[bi:bi + 1, h:h + 1].contiguous(), "hd")
+            vs = mxa.quantize(v[bi:bi + 1, h:h + 1].contiguous(), "key")
+            o1, l1 = mxa.prefill(qs, ks, vs, causal=True, return_lse=True)
+            assert torch.equal(o1[0], out[bi, h * grp:(h + 1) * grp]), (bi, h)
+            assert torch.equal(l1[0], lse[bi, h * grp:(h + 1) * grp]), (bi, h)
+
+
 def test_deterministic_and_launch_order_independent():
     g = torch.Generator(device=DEV).manual_seed(26)
     q = torch.randn((1, 8, 512, 128), generator=g, device=DEV).to(torch.bfloat16)
