@@ -16,9 +16,10 @@
 //               to col_mass.  Each key belongs to exactly one lane: no atomics.
 //   topk     -- per (batch, KV head), one 1024-thread workgroup holding the
 //               masses in registers: the k-th largest fp32 bit pattern found
-//               bit by bit (bit patterns of non-negative values order like the
-//               values), then one ordered compaction that emits the indices
-//               ascending, ties at the threshold going to the lower indices.
+//               by a radix select over 8-bit digits (bit patterns of
+//               non-negative values order like the values), then one ordered
+//               compaction that emits the indices ascending, ties at the
+//               threshold going to the lower indices.
 #include <type_traits>
 
 #include "mx_device.h"
@@ -340,8 +341,9 @@ __device__ __forceinline__ int block_scan_incl(int x, int* wtot) {
 template <int kTopkChunks>   // register capacity: kTopkChunks x 4096 keys
 __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectArgs a) {
   __shared__ int wtot[kTopkWaves];
+  __shared__ uint32_t hist[kTopkWaves][256];
   __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
+  __shared__ int s_krem, s_digit, s_above;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv;
   const int ctx = clamp_ctx(a, b);
@@ -368,36 +370,48 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectArgs a)
       const int i = c * kTopkThreads * 4 + tid * 4 + u;
       x[c][u] = (c < nch && i < n) ? v[i] : 0u;
     }
-  // Threshold: the largest bit pattern tau with at least k entries >= tau,
-  // found bit by bit from the top (fp32 bit patterns of non-negative values
-  // order like the values); each step is one count over the registers.
-  auto count_ge = [&](uint32_t cand) -> int {
-    int c = 0;
-#pragma unroll
-    for (int cc = 0; cc < kTopkChunks; ++cc) {
-      if (cc >= nch) break;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = cc * kTopkThreads * 4 + tid * 4 + u;
-        c += (i < n && x[cc][u] >= cand) ? 1 : 0;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-    if (lane == 0) wtot[wave] = c;
-    __syncthreads();
-    int total = 0;
-    for (int w = 0; w < kTopkWaves; ++w) total += wtot[w];
-    __syncthreads();
-    return total;
-  };
+  // Threshold: the k-th largest fp32 bit pattern tau (bit patterns of
+  // non-negative values order like the values; any other pattern is ordered
+  // as an unsigned integer, so exactly k entries are always taken).  Radix
+  // select, 8 bits per pass from the top: each pass counts, among the
+  // entries whose higher digits equal tau's, how many take each value of the
+  // next digit (wave-private LDS histograms), then takes the digit at which
+  // the count from the top reaches k.  `above` counts the entries already
+  // known to exceed tau.
   uint32_t tau_bits = 0;
+  int above = 0;
   if (k > 0) {
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = tau_bits | (1u << bit);
-      if (count_ge(cand) >= k) tau_bits = cand;
+    uint32_t pmask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int e = tid; e < kTopkWaves * 256; e += kTopkThreads) hist[e >> 8][e & 255] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int cc = 0; cc < kTopkChunks; ++cc) {
+        if (cc >= nch) break;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = cc * kTopkThreads * 4 + tid * 4 + u;
+          if (i < n && (x[cc][u] & pmask) == tau_bits) atomicAdd(&hist[wave][(x[cc][u] >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      // Thread t < 256 owns digit 255 - t, so its inclusive scan is the
+      // count of entries at or above that digit.
+      int cnt = 0;
+      if (tid < 256) {
+        for (int w = 0; w < kTopkWaves; ++w) cnt += static_cast<int>(hist[w][255 - tid]);
+      }
+      const int incl = block_scan_incl(cnt, wtot);
+      if (tid < 256 && above + incl - cnt < k && above + incl >= k) {
+        s_digit = 255 - tid;
+        s_above = above + incl - cnt;
+      }
+      __syncthreads();
+      tau_bits |= static_cast<uint32_t>(s_digit) << shift;
+      pmask |= 255u << shift;
+      above = s_above;
+      __syncthreads();
     }
-    const int above = tau_bits == 0x7FFFFFFFu ? 0 : count_ge(tau_bits + 1);
     if (tid == 0) {
       s_prefix = tau_bits;
       s_krem = k - above;

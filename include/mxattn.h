@@ -333,7 +333,10 @@ mxattn_status_t mxattn_decode_paged(const mxattn_mx_t* q, const mxattn_mx_t* q_r
  *            softmax_scale * q_hat.k_hat_t', for t < ctx.
  *   Then k = ceil((ctx-window) * rho_num / rho_den) (integer arithmetic)
  *   tokens of [0, ctx-window) with the largest mass (ties to the lower index)
- *   are written ascending to idx_out [B][Hkv][max_sel]; n_out [B][Hkv] = k.
+ *   are written ascending to idx_out [B][Hkv][max_sel]; n_out [B][Hkv] = k;
+ *   the remaining entries of idx_out are -1.  Masses are ordered by their
+ *   fp32 bit patterns as unsigned integers, which is their value order when
+ *   they are non-negative; exactly k indices are written whatever the bits.
  *   q_recent may be NULL (R = 0): col_mass is left unchanged and only the
  *   selection runs.
  *   workspace  device memory of mxattn_select_workspace_bytes(...) bytes.

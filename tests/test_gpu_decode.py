@@ -385,6 +385,38 @@ def test_topk_exact_on_given_masses(tcap):
             assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
 
 
+@pytest.mark.parametrize("kind", ["equal", "near_equal", "uniform", "zeros", "rho0"])
+def test_topk_exact_on_edge_masses(kind):
+    """R = 0, top-k only, indices equal to the oracle's: every mass equal (all
+    ties), masses that differ only in their lowest mantissa bits (the
+    threshold is decided by the last byte), uniform floats, all zeros, and
+    rho = 0 (nothing selected)."""
+    rng = np.random.default_rng(43)
+    b, hkv, tcap = 2, 2, 9000
+    if kind == "equal":
+        cm = np.full((b, hkv, tcap), 0.375, dtype=np.float32)
+    elif kind == "near_equal":
+        base = np.float32(1.0).view(np.uint32)
+        cm = (base + rng.integers(0, 700, size=(b, hkv, tcap)).astype(np.uint32)).view(np.float32)
+    elif kind == "uniform":
+        cm = rng.uniform(0, 3, size=(b, hkv, tcap)).astype(np.float32)
+    else:
+        cm = np.zeros((b, hkv, tcap), dtype=np.float32)
+    num = 0 if kind == "rho0" else 7
+    ctx = np.array([tcap, 4000], dtype=np.int32)
+    kc = mxa.empty_mx((b, hkv, tcap, 128), "hd", DEV)
+    col = torch.from_numpy(cm).to(DEV)
+    idx, n = mxa.select_vertical(None, kc, torch.from_numpy(ctx).to(DEV), col, window=64,
+                                 rho_num=num, rho_den=100)
+    torch.cuda.synchronize()
+    for bb in range(b):
+        for h in range(hkv):
+            want = select.topk_vertical(cm[bb, h], int(ctx[bb]), 64, num, 100)
+            got = idx[bb, h, : int(n[bb, h])].cpu().numpy()
+            np.testing.assert_array_equal(got, want, err_msg=f"{kind} b{bb} h{h}")
+            assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
+
+
 def _check_selection(gpu_idx, gpu_n, oracle_cm, ctx, window, num, den, what):
     k, nn = select.n_select(ctx, window, num, den)
     assert gpu_n == k, f"{what}: count {gpu_n} vs {k}"
