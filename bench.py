@@ -281,12 +281,16 @@ def decode_leg(args, flush):
     out = torch.empty((B, HQ, D), dtype=torch.float32, device="cuda")
     q4 = d["q"][:, :, None, :]
 
-    def call():
-        mxa.decode(qh, kc, vc, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
+    qbf = d["q"].contiguous()
 
-    def step():
+    # One call per token: the scan encodes the bf16 query itself.
+    def call():
+        mxa.decode(qbf, kc, vc, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
+
+    # The same step as two launches: the quantiser, then the scan on its codes.
+    def step_two_launches():
         mxa.quantize(q4, "hd", out=qh)
-        call()
+        mxa.decode(qh, kc, vc, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
 
     # The same decode with a dual-residual query (two MXFP4 query halves,
     # one more QK^T MFMA per chunk).
@@ -301,7 +305,8 @@ def decode_leg(args, flush):
         call_dual()
 
     t_call = timed_flushed(call, args.steps, args.warmup, flush)
-    t_step = timed_flushed(step, args.steps, args.warmup, flush)
+    t_step = t_call
+    t_step2 = timed_flushed(step_two_launches, args.steps, args.warmup, flush)
     t_call_d = timed_flushed(call_dual, args.steps, args.warmup, flush)
     t_step_d = timed_flushed(step_dual, args.steps, args.warmup, flush)
 
@@ -326,7 +331,7 @@ def decode_leg(args, flush):
     torch.cuda.empty_cache()
 
     def call_paged():
-        mxa.decode_paged(qh, kp, vp, table, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
+        mxa.decode_paged(qbf, kp, vp, table, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
 
     t_call_p = timed_flushed(call_paged, args.steps, args.warmup, flush)
     cache_bytes = B * HKV * T * (D // 2 + D // 32) * 2
@@ -335,8 +340,10 @@ def decode_leg(args, flush):
     alg_d = alg + q_bytes
     return {
         "workload": "batch 32, 32/8 heads, head_dim 128, ctx 32768, MXFP4 K/V cache (E2M1 + E8M0 per 32 "
-                    f"along head_dim), MXFP4 query, split {SPLIT}; step = quantise q + decode (scan + merge)",
+                    f"along head_dim), MXFP4 query, split {SPLIT}; step = one decode call (the scan encodes the "
+                    "bf16 query, then the merge)",
         "ms_per_token": round(t_step * 1e3, 4),
+        "ms_per_token_two_launches": round(t_step2 * 1e3, 4),
         "GB_per_s": round(alg / t_step / 1e9, 1),
         "algorithmic_bytes": alg,
         "roofline": {"bound": "hbm", "kernel": "mxattn_decode (decode_scan_kernel<128> + merge)",
@@ -393,15 +400,17 @@ def hybrid_leg(args, flush):
     q4 = d["q"][:, :, None, :]
     qbf = d["q"].contiguous()
 
+    # One call per token: the scan encodes the bf16 query for the 4-bit tokens.
     def call():
+        mxa.decode(qbf, kc, vc, d["ctx_len"], split_len=SPLIT, hybrid=hy, workspace=ws, out=out)
+
+    def step_two_launches():
+        mxa.quantize(q4, "hd", out=qh)
         mxa.decode(qh, kc, vc, d["ctx_len"], split_len=SPLIT, hybrid=hy, q_bf16=qbf, workspace=ws, out=out)
 
-    def step():
-        mxa.quantize(q4, "hd", out=qh)
-        call()
-
     t_call = timed_flushed(call, args.steps, args.warmup, flush)
-    t_step = timed_flushed(step, args.steps, args.warmup, flush)
+    t_step = t_call
+    t_step2 = timed_flushed(step_two_launches, args.steps, args.warmup, flush)
     t_sel = timed_flushed(select, max(args.steps // 4, 3), 1, flush)
     nsel = int(n[0, 0].item())
     n4 = T - W - nsel
@@ -410,8 +419,9 @@ def hybrid_leg(args, flush):
     return {
         "workload": "batch 8, 32/8 heads, head_dim 128, ctx 32768, heavy-tailed column bias; 1632 selected "
                     "(top 5% of the non-window prefix by column mass) + 128-token window in bf16, rest MXFP4, "
-                    f"one softmax, split {SPLIT}; step = quantise q + hybrid decode",
+                    f"one softmax, split {SPLIT}; step = one hybrid decode call (the scan encodes the bf16 query)",
         "ms_per_token": round(t_step * 1e3, 4),
+        "ms_per_token_two_launches": round(t_step2 * 1e3, 4),
         "GB_per_s": round(alg / t_step / 1e9, 1),
         "algorithmic_bytes": alg,
         "bf16_overhead_of_nonwindow_kv": round(nsel * (2 * D * 2 - (D // 2 + D // 32) * 2) /

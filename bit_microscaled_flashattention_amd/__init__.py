@@ -169,12 +169,15 @@ class MX:
     layout: str = "hd"
 
     def desc(self):
+        """C descriptor; an MX without codes (None) describes only a shape."""
         b, h, s, d = self.shape
         c, sc = self.codes, self.scales
         m = _Mx()
-        m.codes, m.scales = c.data_ptr(), sc.data_ptr()
         m.batch, m.heads, m.seq, m.dim = b, h, s, d
         m.layout = LAYOUT_HD if self.layout == "hd" else LAYOUT_KEY
+        if c is None:
+            return m
+        m.codes, m.scales = c.data_ptr(), sc.data_ptr()
         for i in range(3):
             m.code_stride[i] = c.stride(i) * c.element_size()
             m.scale_stride[i] = sc.stride(i) * sc.element_size()
@@ -333,7 +336,9 @@ def decode(q, k_cache, v_cache, ctx_len, softmax_scale=0.0, split_len=2048, hybr
            q_bf16=None, workspace=None, return_lse=False, out=None, q_res=None):
     """One query token per sequence against an MXFP4 KV cache.
 
-    q: MX [B,Hq,1,D]; caches: MX [B,Hkv,Tcap,D]; ctx_len int32 [B] on device.
+    q: MX [B,Hq,1,D], or a bfloat16 tensor [B,Hq,D] / [B,Hq,1,D] that the scan
+    encodes itself (OCP, the codes quantize() writes); caches: MX
+    [B,Hkv,Tcap,D]; ctx_len int32 [B] on device.
     hybrid: None or dict(idx, n_sel, k_sel, v_sel, k_win, v_win, window).
     q_res: None or the residual MX of a dual-residual query (quantize_dual).
     """
@@ -354,9 +359,17 @@ def decode_paged(q, k_pool, v_pool, block_table, ctx_len, softmax_scale=0.0, spl
 
 def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, q_bf16, workspace, return_lse,
             out, q_res):
+    if isinstance(q, torch.Tensor):
+        # bf16 query [B,Hq,D] or [B,Hq,1,D]: the scan encodes it (OCP), no
+        # separate quantiser launch.
+        assert q.dtype == torch.bfloat16, "an unencoded query must be bfloat16"
+        qb = q.reshape(q.shape[0], q.shape[1], q.shape[-1]).contiguous()
+        assert q_bf16 is None or q_bf16.data_ptr() == qb.data_ptr(), "pass the bf16 query once, as q"
+        q_bf16 = qb
+        q = MX(None, None, (qb.shape[0], qb.shape[1], 1, qb.shape[2]), "hd")
     b, hq, _, d = q.shape
     hkv = kc.shape[1]
-    dev = q.codes.device
+    dev = kc.codes.device
     hy_rows = (hybrid["idx"].shape[-1] + int(hybrid["window"])) if hybrid is not None else 0
     need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hy_rows)
     if workspace is None or workspace.numel() < need:
@@ -377,7 +390,7 @@ def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, 
     dqr = q_res.desc() if q_res is not None else None
     common = (ctypes.byref(dqr) if dqr is not None else None, _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv))
     tail = (_ptr(ctx_len), ctypes.byref(hy) if hy is not None else None, float(softmax_scale), int(split_len),
-            _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(q.codes))
+            _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(kc.codes))
     if paging is None:
         _check(_lib.mxattn_decode(ctypes.byref(dq), *common, *tail))
     else:

@@ -395,7 +395,20 @@ static mxattn_status_t decode_common(const mxattn_mx_t* q, const mxattn_mx_t* q_
                                      int32_t split_len, void* workspace, size_t workspace_bytes, float* out,
                                      float* lse, mxattn_stream_t stream) {
   mxattn_status_t st;
-  if ((st = check_mx(q, "decode.q", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
+  // A query descriptor without codes and scales gives only the shape: the
+  // scan encodes q_bf16 itself.
+  const bool q_fused = q != nullptr && q->codes == nullptr && q->scales == nullptr;
+  if (q_fused) {
+    if (q_bf16 == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode: q without codes needs q_bf16 to encode");
+    if (q_res != nullptr) return fail(MXATTN_ERR_UNSUPPORTED, "decode: a dual-residual query must come encoded");
+    if (!aligned16(q_bf16)) return fail(MXATTN_ERR_INVALID_ARG, "decode: q_bf16 not 16-byte aligned");
+    if (q->layout != MXATTN_LAYOUT_HD) return fail(MXATTN_ERR_UNSUPPORTED, "decode.q: layout must be HD");
+    if (q->batch < 1 || q->heads < 1 || q->seq < 1) return fail(MXATTN_ERR_INVALID_ARG, "decode.q: empty shape");
+    if (q->dim != 64 && q->dim != 128) return fail(MXATTN_ERR_UNSUPPORTED, "decode.q: head_dim not in {64,128}");
+    if (q->batch > 65535 || q->heads > 65535) return fail(MXATTN_ERR_UNSUPPORTED, "decode.q: batch/heads above 65535");
+  } else if ((st = check_mx(q, "decode.q", MXATTN_LAYOUT_HD)) != MXATTN_OK) {
+    return st;
+  }
   if ((st = check_mx(kc, "decode.k_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if ((st = check_mx(vc, "decode.v_cache", MXATTN_LAYOUT_HD)) != MXATTN_OK) return st;
   if (ctx_len == nullptr || out == nullptr) return fail(MXATTN_ERR_INVALID_ARG, "decode: null ctx_len/out");
@@ -483,8 +496,9 @@ static mxattn_status_t decode_common(const mxattn_mx_t* q, const mxattn_mx_t* q_
   a.out = out;
   a.lse = lse;
   a.hybrid = hybrid;
+  a.q_fused = q_fused;
+  if (hybrid || q_fused) a.q_bf16 = static_cast<const uint16_t*>(q_bf16);
   if (hybrid) {
-    a.q_bf16 = static_cast<const uint16_t*>(q_bf16);
     a.idx = hy->idx;
     a.n_sel = hy->n_sel;
     a.max_sel = hy->max_sel;

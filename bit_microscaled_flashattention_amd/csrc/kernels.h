@@ -119,7 +119,8 @@ struct DecodeArgs {
   float* lse;
   // hybrid
   int hybrid;
-  const uint16_t* q_bf16;
+  const uint16_t* q_bf16;   // bf16 [B][Hq][D]: the hybrid set's query, and the source of q when q_fused
+  int q_fused;              // q is encoded from q_bf16 inside the scan (OCP rule)
   const int32_t* idx;
   const int32_t* n_sel;
   int max_sel, window;

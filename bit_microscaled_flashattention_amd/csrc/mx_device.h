@@ -98,4 +98,25 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 2^(byte-127) as an fp32 scale for the convert instructions (byte >= 1).
 __device__ __forceinline__ float scale_of_byte(int b) { return __uint_as_float(static_cast<uint32_t>(b) << 23); }
 
+// Eight elements to eight packed E2M1 codes (element i in nibble i) under
+// scale byte sb.  From byte 3 up the hardware convert does it: it rounds
+// y/2^e to nearest even on the E2M1 grid, saturates and keeps the sign, and
+// every fp32 subnormal element lands below 0.25 and codes to signed zero
+// whatever the convert's denormal handling.  Bytes 0..2 take the
+// integer-exact encoder.
+__device__ __forceinline__ uint32_t encode8(const float* y, int sb) {
+  uint32_t packed = 0;
+  if (sb >= 3) {
+    const float scl = scale_of_byte(sb);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], scl, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], scl, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], scl, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], scl, 3);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_code(y[i], sb) << (4 * i);
+  }
+  return packed;
+}
+
 }  // namespace mxattn

@@ -43,28 +43,6 @@ __device__ __forceinline__ void load8(const void* base, int64_t i, float* y) {
 }
 
 // ---------------------------------------------------------------------------
-// Eight elements to eight packed E2M1 codes (element i in nibble i) under
-// scale byte sb.  From byte 3 up the hardware convert does it: it rounds
-// y/2^e to nearest even on the E2M1 grid, saturates and keeps the sign, and
-// every fp32 subnormal element lands below 0.25 and codes to signed zero
-// whatever the convert's denormal handling.  Bytes 0..2 take the
-// integer-exact encoder.
-__device__ __forceinline__ uint32_t encode8(const float* y, int sb) {
-  uint32_t packed = 0;
-  if (sb >= 3) {
-    const float scl = scale_of_byte(sb);
-    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], scl, 0);
-    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], scl, 1);
-    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], scl, 2);
-    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], scl, 3);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_code(y[i], sb) << (4 * i);
-  }
-  return packed;
-}
-
-// ---------------------------------------------------------------------------
 // Head-dim blocks.  Four lanes own one 32-element block (8 elements each, one
 // 16-byte load for 16-bit inputs), so one load instruction of a wave covers
 // 16 consecutive blocks contiguously.  Each lane handles kHdRows such

@@ -242,12 +242,17 @@ mxattn_status_t mxattn_prefill_hybrid(const mxattn_mx_t* q, const mxattn_mx_t* k
  * mxattn_decode -- one query token per sequence against an MXFP4 KV cache,
  * dequantisation fused into the scan, optionally with a bf16 hybrid token set
  * under the same softmax (HyQuant, method paragraphs).
- *   q        HD layout [B][Hq][1][D] (MXFP4 query).
+ *   q        HD layout [B][Hq][1][D] (MXFP4 query).  Or a descriptor with
+ *            codes and scales NULL, which gives only the shape: the scan then
+ *            encodes q_bf16 itself (OCP rule, no channel factors), with the
+ *            codes mxattn_quantize would write, so one call does the step.
  *   q_res    nullable; HD layout, same shape: the residual part of a
  *            dual-residual query (mxattn_quantize_dual).  The 4-bit logits
  *            then use dequant(q) + dequant(q_res) (one more QK^T MFMA per
- *            chunk); the bf16 hybrid tokens keep using q_bf16.
- *   q_bf16   bf16 [B][Hq][D] contiguous; read only when hybrid != NULL.
+ *            chunk); the bf16 hybrid tokens keep using q_bf16.  Needs an
+ *            encoded q.
+ *   q_bf16   bf16 [B][Hq][D] contiguous, 16-byte aligned; read when hybrid
+ *            != NULL or when q comes without codes.
  *   k_cache, v_cache  HD layout [B][Hkv][Tcap][D].
  *   ctx_len  device int32 [B]; token t of sequence b is attended iff
  *            t < ctx_len[b] (1 <= ctx_len[b] <= Tcap, checked on the device:

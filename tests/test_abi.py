@@ -388,3 +388,21 @@ def test_header_is_plain_c_and_links(tmp_path):
     st, text, version, ws = out.stdout.strip().split("|")
     assert int(st) == 1 and "invalid" in text and "gfx950" in version
     assert int(ws) == mxa.decode_workspace_bytes(32, 32, 8, 128, 32768, 4096)
+
+
+def test_decode_unencoded_query_rejects():
+    """A query descriptor without codes needs q_bf16 and cannot carry a
+    dual-residual half; both are refused on the host."""
+    lib = mxa.library()
+    q = _mx(codes=None, scales=None, b=2, h=8, s=1, d=128)
+    k = _mx(b=2, h=2, s=256, d=128)
+    out = ctypes.c_void_p(16)
+    ctx = ctypes.c_void_p(16)
+    ws = ctypes.c_void_p(256)
+    st = lib.mxattn_decode(ctypes.byref(q), None, None, ctypes.byref(k), ctypes.byref(k), ctx, None, 0.0, 256,
+                           ws, 1 << 20, out, None, None)
+    assert st == 1 and b"q_bf16" in lib.mxattn_last_error()
+    qr = _mx(b=2, h=8, s=1, d=128)
+    st = lib.mxattn_decode(ctypes.byref(q), ctypes.byref(qr), ctypes.c_void_p(16), ctypes.byref(k), ctypes.byref(k),
+                           ctx, None, 0.0, 256, ws, 1 << 20, out, None, None)
+    assert st == 2 and b"dual" in lib.mxattn_last_error()

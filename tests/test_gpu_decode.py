@@ -252,6 +252,38 @@ def test_decode_paged_hybrid_and_dual_query():
     assert torch.equal(ref, got)
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(128, 32, 8), (64, 8, 8), (128, 16, 2)])
+def test_decode_encodes_bf16_query_in_scan(d, hq, hkv):
+    """A bf16 query handed to the scan unencoded gives the bits of the same
+    decode on the quantiser's codes: plain, hybrid and paged scans.  Queries
+    carry outlier channels and tiny blocks so several scale bytes, including
+    the integer encoder's range, occur."""
+    g = torch.Generator(device=DEV).manual_seed(46)
+    b, tcap, page = 3, 4096, 64
+    qf = torch.randn((b, hq, d), generator=g, device=DEV)
+    qf[:, :, 5] *= 40
+    qf[0, 0, :32] *= 1e-38
+    q = qf.to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([4096, 1777, 40], dtype=torch.int32, device=DEV)
+    kc, vc = _cache(k, v)
+    qh = mxa.quantize(q[:, :, None, :], "hd")
+    print(f"decode with the query encoded in the scan d={d} hq={hq} hkv={hkv}", flush=True)
+    ref_o, ref_l = mxa.decode(qh, kc, vc, ctx, split_len=1024, return_lse=True)
+    got_o, got_l = mxa.decode(q, kc, vc, ctx, split_len=1024, return_lse=True)
+    hy, _ = _hybrid_inputs(q, k, v, ctx, 64, 50, 64, seed=11)
+    ref_h = mxa.decode(qh, kc, vc, ctx, split_len=1024, hybrid=hy, q_bf16=q.contiguous())
+    got_h = mxa.decode(q, kc, vc, ctx, split_len=1024, hybrid=hy)
+    kp, table = _page_pool(kc, page, ctx, seed=5)
+    vp, _ = _page_pool(vc, page, ctx, seed=5)
+    got_p = mxa.decode_paged(q[:, :, None, :], kp, vp, table, ctx, split_len=1024)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_o, got_o) and torch.equal(ref_l, got_l)
+    assert torch.equal(ref_h, got_h)
+    assert torch.equal(ref_o, got_p)
+
+
 def _hybrid_inputs(q, k, v, ctx, window, n_sel, max_sel, seed):
     """Seeded selected sets (ascending, below ctx-window) and the gathered
     bf16 rows the decode reads."""
