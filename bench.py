@@ -38,10 +38,11 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # fetch 6894 KiB x 2.000 + write 65545 KiB x 1.000 per dispatch (medians of 10)
-    "prefill_kernel<128,128,true,true>": {"bytes": 81236992, "sources": "4305e8bbeea2ca69"},
-    # fetch 557403 KiB x 2.000 + write 4352 KiB x 1.000 per dispatch (medians of 6)
-    "decode_scan_kernel<128> split 4096": {"bytes": 1146017792, "sources": "8b7c65ef8be1cbed"},
+    # fetch 6895 KiB x 2.000 + write 65546.5 KiB x 1.000 per dispatch (medians of 10)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81240576, "sources": "add57e897951e022"},
+    # the one-call step (bf16 query encoded in the scan): fetch 558212 KiB x 2.000
+    # + write 4352 KiB x 1.000 per dispatch (medians of 3)
+    "decode_scan_kernel<128> split 4096": {"bytes": 1147674624, "sources": "c49a6b596222ac8b"},
 }
 TRAFFIC_SOURCES = {
     "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
@@ -335,9 +336,12 @@ def decode_leg(args, flush):
 
     t_call_p = timed_flushed(call_paged, args.steps, args.warmup, flush)
     cache_bytes = B * HKV * T * (D // 2 + D // 32) * 2
-    q_bytes = B * HQ * (D // 2 + D // 32)
+    # The one-call step reads the bf16 query (the scan encodes it); the dual
+    # call reads both encoded halves.
+    q_bytes = B * HQ * D * 2
+    q_mx_bytes = B * HQ * (D // 2 + D // 32)
     alg = cache_bytes + q_bytes + B * HQ * D * 4
-    alg_d = alg + q_bytes
+    alg_d = cache_bytes + 2 * q_mx_bytes + B * HQ * D * 4
     return {
         "workload": "batch 32, 32/8 heads, head_dim 128, ctx 32768, MXFP4 K/V cache (E2M1 + E8M0 per 32 "
                     f"along head_dim), MXFP4 query, split {SPLIT}; step = one decode call (the scan encodes the "
@@ -415,7 +419,7 @@ def hybrid_leg(args, flush):
     nsel = int(n[0, 0].item())
     n4 = T - W - nsel
     per_pair = n4 * (D // 2 + D // 32) * 2 + (nsel + W) * D * 2 * 2 + nsel * 4
-    alg = B * HKV * per_pair + B * HQ * (D // 2 + D // 32 + 2 * D) + B * HQ * D * 4
+    alg = B * HKV * per_pair + B * HQ * 2 * D + B * HQ * D * 4     # bf16 query read once per head
     return {
         "workload": "batch 8, 32/8 heads, head_dim 128, ctx 32768, heavy-tailed column bias; 1632 selected "
                     "(top 5% of the non-window prefix by column mass) + 128-token window in bf16, rest MXFP4, "
