@@ -81,8 +81,9 @@ mxattn_status_t check_mx(const mxattn_mx_t* t, const char* name, int want_layout
     return fail(MXATTN_ERR_INVALID_ARG, "%s: empty shape [%lld,%lld,%lld,%lld]", name, (long long)t->batch,
                 (long long)t->heads, (long long)t->seq, (long long)t->dim);
   if (t->dim != 64 && t->dim != 128) return fail(MXATTN_ERR_UNSUPPORTED, "%s: head_dim %lld not in {64,128}", name, (long long)t->dim);
-  // Batch and heads index grid dimensions y and z; positions inside one head
-  // are 32-bit in the kernels.
+  // Batch and heads index grid dimensions of some launches (the decode merge,
+  // the selection kernels), which allow up to 65535; positions inside one
+  // head are 32-bit in the kernels.
   if (t->batch > 65535 || t->heads > 65535 || t->seq > (int64_t{1} << 26))
     return fail(MXATTN_ERR_UNSUPPORTED, "%s: batch/heads above 65535 or seq above 2^26", name);
   if (!aligned16(t->codes)) return fail(MXATTN_ERR_INVALID_ARG, "%s: codes not 16-byte aligned", name);
