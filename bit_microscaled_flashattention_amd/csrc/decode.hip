@@ -257,14 +257,38 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
   v4i qop = {0, 0, 0, 0}, qop2 = {0, 0, 0, 0};
   int qsc = 0, qsc2 = 0;
   // Encoded in the scan (q_fused): the lane's 32 bf16 query values are
-  // loaded here, before the first chunks' loads, and encoded after those are
-  // issued (see below), so their wait covers the query load alone.
+  // loaded here, before the first chunks' loads.  One 32-channel block per
+  // lane, the quantiser's rule (OCP) and encoder: the codes mxattn_quantize
+  // writes.  The contiguous scan encodes after its first chunk loads are
+  // issued, so their wait covers the query load alone; the paged scan
+  // encodes here, which measured faster there (its first loads wait on the
+  // block table anyway).
   v4i qraw[4] = {};
   const bool q_lane = j < G && g < D / 32;
+  auto encode_q = [&]() {
+    float y[32];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = static_cast<uint32_t>(qraw[c4][e]);
+        y[8 * c4 + 2 * e] = __uint_as_float(u << 16);
+        y[8 * c4 + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t mg = __float_as_uint(y[i]) & 0x7FFFFFFFu;
+      amax = mg > amax ? mg : amax;
+    }
+    qsc = e8m0_byte(amax, false, 0.0f);
+    qop = v4i{(int)encode8(y, qsc), (int)encode8(y + 8, qsc), (int)encode8(y + 16, qsc), (int)encode8(y + 24, qsc)};
+  };
   if (q_lane && a.q_fused) {
     const uint16_t* src = a.q_bf16 + (static_cast<int64_t>(b) * a.Hq + hk * G + j) * D + g * 32;
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) qraw[c4] = *reinterpret_cast<const v4i*>(src + 8 * c4);
+    if constexpr (PAGED) encode_q();
   } else if (j < G && g < D / 32) {
     const int hq = hk * G + j;
     const uint8_t* qc = a.q.codes + b * a.q.cs[0] + hq * a.q.cs[1];
@@ -392,26 +416,8 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
   __builtin_amdgcn_sched_barrier(0);
   load(B, chunk_t0(1));
   __builtin_amdgcn_sched_barrier(0);
-  if (q_lane && a.q_fused) {
-    // One 32-channel block per lane, the quantiser's rule (OCP) and encoder:
-    // the codes mxattn_quantize writes.
-    float y[32];
-    uint32_t amax = 0;
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = static_cast<uint32_t>(qraw[c4][e]);
-        y[8 * c4 + 2 * e] = __uint_as_float(u << 16);
-        y[8 * c4 + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
-      }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t mg = __float_as_uint(y[i]) & 0x7FFFFFFFu;
-      amax = mg > amax ? mg : amax;
-    }
-    qsc = e8m0_byte(amax, false, 0.0f);
-    qop = v4i{(int)encode8(y, qsc), (int)encode8(y + 8, qsc), (int)encode8(y + 16, qsc), (int)encode8(y + 24, qsc)};
+  if constexpr (!PAGED) {
+    if (q_lane && a.q_fused) encode_q();
   }
   for (int i = 0; i < mine; i += 2) {
     process(A, chunk_t0(i));
