@@ -40,9 +40,9 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 PROFILED_TRAFFIC = {
     # fetch 6895 KiB x 2.000 + write 65546.5 KiB x 1.000 per dispatch (medians of 10)
     "prefill_kernel<128,128,true,true>": {"bytes": 81240576, "sources": "add57e897951e022"},
-    # the one-call step (bf16 query encoded in the scan): fetch 558221 KiB x 2.000
+    # the one-call step (bf16 query encoded in the scan): fetch 558213 KiB x 2.000
     # + write 4352 KiB x 1.000 per dispatch (medians of 3)
-    "decode_scan_kernel<128> split 4096": {"bytes": 1147693056, "sources": "8115bc167f4d7fbc"},
+    "decode_scan_kernel<128> split 4096": {"bytes": 1147676672, "sources": "70340a3ff903639e"},
 }
 TRAFFIC_SOURCES = {
     "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
