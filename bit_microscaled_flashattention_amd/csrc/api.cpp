@@ -346,10 +346,10 @@ static mxattn_status_t prefill_common(const mxattn_mx_t* q, const mxattn_mx_t* k
     a.max_sel = hy->max_sel;
     a.window = hy->window;
   }
-  // Paired schedule: a causal 4-bit launch whose query blocks, two per
-  // workgroup, make exactly one round of two workgroups per CU (kv_tile 256
-  // holds one workgroup per CU), with whole KV heads per XCD.
-  if (hy == nullptr && p->causal && kv_tile != 256 && a.n_qblk >= 4 && a.n_qblk % 4 == 0 &&
+  // Paired schedule: a causal launch (plain or hybrid) whose query blocks,
+  // two per workgroup, make exactly one round of two workgroups per CU
+  // (kv_tile 256 holds one workgroup per CU), with whole KV heads per XCD.
+  if (p->causal && kv_tile != 256 && a.n_qblk >= 4 && a.n_qblk % 4 == 0 &&
       (a.B * a.Hkv) % 8 == 0) {
     const int n_cu = device_cu_count();
     if (n_cu > 0 && static_cast<int64_t>(a.n_qblk) * a.B * a.Hq == 4LL * n_cu) {

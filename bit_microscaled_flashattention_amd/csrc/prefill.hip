@@ -849,7 +849,7 @@ __global__ __launch_bounds__(kThreads, (BC == 256 ? 1 : 2)) void prefill_kernel(
   // (those past the last row belong to empty blocks and are never used).
   __shared__ __attribute__((aligned(16))) uint32_t selmap[HYB ? kHybSelWords + 8 : 1];
   int qb1, qb2 = -1, b, hq;
-  if (!HYB && CAUSAL && a.paired) map_pair(a, qb1, qb2, b, hq);
+  if (CAUSAL && a.paired) map_pair(a, qb1, qb2, b, hq);
   else map_block(a, CAUSAL, qb1, b, hq);
   prefill_item<D, BC, CAUSAL, LQ, PUOS, HYB>(a, qb1, b, hq, smem, selmap);
   if (qb2 >= 0) {

@@ -199,6 +199,33 @@ def test_causal_schedule_matches_per_head_launches(shape):
             assert torch.equal(l1[0], lse[bi, h * grp:(h + 1) * grp]), (bi, h)
 
 
+def test_hybrid_causal_schedule_matches_per_head_launches():
+    """The hybrid prefill on the paired schedule (4K, 32/8 heads: one round
+    of two workgroups per CU) equals, bit for bit, separate hybrid launches
+    over each KV head's group."""
+    b, hq, hkv, s, w, n_sel = 1, 32, 8, 4096, 128, 150
+    g = torch.Generator(device=DEV).manual_seed(31)
+    print("paired schedule, hybrid prefill 4K", flush=True)
+    q = torch.randn((b, hq, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, s, 128), generator=g, device=DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(31)
+    idx = torch.from_numpy(np.stack([np.sort(rng.choice(s - w, size=n_sel, replace=False))
+                                     for _ in range(hkv)]).astype(np.int32)[None]).to(DEV)
+    nsel = torch.full((b, hkv), n_sel, dtype=torch.int32, device=DEV)
+    qh, kh, vh = mxa.quantize(q, "hd"), mxa.quantize(k, "hd"), mxa.quantize(v, "key")
+    out, lse = mxa.prefill_hybrid(qh, kh, vh, q, k, v, w, idx, nsel, return_lse=True)
+    grp = hq // hkv
+    for h in range(hkv):
+        qs_ = q[:, h * grp:(h + 1) * grp].contiguous()
+        ks_, vs_ = k[:, h:h + 1].contiguous(), v[:, h:h + 1].contiguous()
+        o1, l1 = mxa.prefill_hybrid(mxa.quantize(qs_, "hd"), mxa.quantize(ks_, "hd"), mxa.quantize(vs_, "key"),
+                                    qs_, ks_, vs_, w, idx[:, h:h + 1].contiguous(), nsel[:, h:h + 1].contiguous(),
+                                    return_lse=True)
+        assert torch.equal(o1[0], out[0, h * grp:(h + 1) * grp]), h
+        assert torch.equal(l1[0], lse[0, h * grp:(h + 1) * grp]), h
+
+
 def test_deterministic_and_launch_order_independent():
     g = torch.Generator(device=DEV).manual_seed(26)
     q = torch.randn((1, 8, 512, 128), generator=g, device=DEV).to(torch.bfloat16)
