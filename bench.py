@@ -38,8 +38,8 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # fetch 6895 KiB x 2.000 + write 65546.5 KiB x 1.000 per dispatch (medians of 10)
-    "prefill_kernel<128,128,true,true>": {"bytes": 81240576, "sources": "add57e897951e022"},
+    # fetch 6884.1 KiB x 2.000 + write 65540.0 KiB x 1.000 per dispatch (medians of 10)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81211616, "sources": "c93be10ee1f0f879"},
     # the one-call step (bf16 query encoded in the scan): fetch 558213 KiB x 2.000
     # + write 4352 KiB x 1.000 per dispatch (medians of 3)
     "decode_scan_kernel<128> split 4096": {"bytes": 1147676672, "sources": "70340a3ff903639e"},
