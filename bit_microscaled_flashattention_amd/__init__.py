@@ -357,6 +357,32 @@ def decode_paged(q, k_pool, v_pool, block_table, ctx_len, softmax_scale=0.0, spl
                    split_len, hybrid, q_bf16, workspace, return_lse, out, q_res)
 
 
+def _check_hybrid(hy, q_bf16, b, hq, hkv, d):
+    """The C ABI receives the hybrid set as bare pointers: check here that
+    each tensor has the dtype, layout and shape the scan reads."""
+    def need(cond, what):
+        if not cond:
+            raise ValueError(f"decode hybrid: {what}")
+
+    idx, n_sel = hy["idx"], hy["n_sel"]
+    need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.dim() == 3 and tuple(idx.shape[:2]) == (b, hkv),
+         f"idx must be contiguous int32 [{b},{hkv},max_sel], got {idx.dtype} {tuple(idx.shape)}")
+    need(n_sel.dtype == torch.int32 and n_sel.is_contiguous() and tuple(n_sel.shape) == (b, hkv),
+         f"n_sel must be contiguous int32 [{b},{hkv}], got {n_sel.dtype} {tuple(n_sel.shape)}")
+    w = int(hy["window"])
+    rows = {"k_sel": idx.shape[-1], "v_sel": idx.shape[-1]}
+    if w > 0:
+        rows.update(k_win=w, v_win=w)
+    for name, r in rows.items():
+        t = hy.get(name)
+        need(t is not None and t.dtype == torch.bfloat16 and t.is_contiguous() and tuple(t.shape) == (b, hkv, r, d),
+             f"{name} must be contiguous bfloat16 [{b},{hkv},{r},{d}]"
+             + ("" if t is None else f", got {t.dtype} {tuple(t.shape)}"))
+    need(q_bf16 is not None and q_bf16.dtype == torch.bfloat16 and q_bf16.is_contiguous()
+         and q_bf16.numel() == b * hq * d and q_bf16.shape[0] == b and q_bf16.shape[1] == hq,
+         f"q_bf16 must be contiguous bfloat16 [{b},{hq},{d}]")
+
+
 def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, q_bf16, workspace, return_lse,
             out, q_res):
     if isinstance(q, torch.Tensor):
@@ -370,6 +396,8 @@ def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, 
     b, hq, _, d = q.shape
     hkv = kc.shape[1]
     dev = kc.codes.device
+    if hybrid is not None:
+        _check_hybrid(hybrid, q_bf16, b, hq, hkv, d)
     hy_rows = (hybrid["idx"].shape[-1] + int(hybrid["window"])) if hybrid is not None else 0
     need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hy_rows)
     if workspace is None or workspace.numel() < need:

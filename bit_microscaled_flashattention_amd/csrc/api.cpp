@@ -316,6 +316,15 @@ static mxattn_status_t prefill_common(const mxattn_mx_t* q, const mxattn_mx_t* k
   const int64_t grid = ((q->seq + 127) / 128) * q->batch * q->heads;
   if (grid > 0x7FFFFFFF || q->seq > 0x7FFFFFFF || k->seq > 0x7FFFFFFF)
     return fail(MXATTN_ERR_UNSUPPORTED, "prefill: problem too large for one launch");
+  // The kernel reads one (batch, KV head) of K and V through buffer resources
+  // with 32-bit sizes and 32-bit offsets: K rows are visited up to the end of
+  // the last 256-key tile, V channel rows up to 128 bytes past their last block.
+  {
+    const int64_t sk_pad = (k->seq + 255) / 256 * 256;
+    if (sk_pad * k->code_stride[2] > 0x7FFFFFFF || sk_pad * k->scale_stride[2] > 0x7FFFFFFF ||
+        v->dim * v->code_stride[2] + 256 > 0x7FFFFFFF || v->dim * v->scale_stride[2] > 0x7FFFFFFF)
+      return fail(MXATTN_ERR_UNSUPPORTED, "prefill: one head of K or V must span less than 2 GiB");
+  }
   PrefillArgs a{};
   a.q = view_of(q);
   a.k = view_of(k);

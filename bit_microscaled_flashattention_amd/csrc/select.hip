@@ -1,9 +1,9 @@
 // Vertical-line selection for hybrid-precision decode.
 //
-// Method: HyQuant page (method paragraphs) -- the vertical-line score of a key
-// is its accumulated column mass; the top-rho fraction of the non-window
-// prefix is kept in full precision; identification is a light reduction run
-// every 64 tokens.
+// Method: HyQuant page (method paragraphs).  A key's score is the attention
+// probability it has received from the queries decoded since the last call,
+// summed into a per-key total; a call adds to that total and returns the
+// rho fraction of highest-scoring keys before the recent window.
 //
 // Kernels
 //   stats    -- per (2048-key context chunk, batch x KV head): every recent

@@ -188,7 +188,10 @@ mxattn_status_t mxattn_smooth_calibrate(const void* q_cal, const void* k_cal, mx
  *   m + ln l, fp32 [B][Hq][Sq].  Query head g reads KV head g/(Hq/Hkv).
  * Softmax state is fp32; P_hat never leaves registers.
  * Supported: D in {64,128}; kv_tile in {64,128,256}; causal needs Sq == Sk;
- * Hq % Hkv == 0; p_qmax in (4, 8) for UOS. */
+ * Hq % Hkv == 0; p_qmax in (4, 8) for UOS; one (batch, KV head) of K spans
+ * less than 2 GiB (Sk rounded up to 256 rows x row stride, codes and scales
+ * alike) and so does one of V (D x row stride); MXATTN_ERR_UNSUPPORTED
+ * otherwise. */
 typedef struct {
   int32_t causal;
   float softmax_scale;      /* 0 selects 1/sqrt(D) */

@@ -62,8 +62,15 @@ in its two limits; hybrid prefill reduces to the 4-bit prefill (empty set,
 window 0) and to textbook attention on the full-precision rows (window >= Sq),
 equals textbook attention for any window and set when P is not quantised and
 both operand sets coincide (every key counted once), and matches a direct
-whole-row computation when one tile spans the sequence.  Attention values under quantisation have no worked
-example in the sources: beyond those invariants they are "parity unpinned".
+whole-row computation when one tile spans the sequence.  Across tiles, the
+hand-worked two-tile table tests/golden/two_tile_running_max.txt fixes the
+reference maximum (the running one, after the tile), the rescale of earlier
+tiles and both normaliser rules under both scale rules.  The multi-head
+wrappers prefill and decode are pinned against the repeat-each-KV-head form
+of grouped-query attention (np.repeat along the head axis) with textbook
+softmax, the direct whole-row PNQ and substituted hybrid rows.  Attention
+values under quantisation on general inputs have no worked example in the
+sources: beyond those cases and invariants they rest on the steps above.
 """
 
 import numpy as np

@@ -26,7 +26,9 @@ Readings taken where the sources are silent:
 
 Parity: pinned by tests/test_oracle_codec.py (closed forms, exhaustive bf16
 enumeration against an independent threshold formulation, round trips, the
-OCP/UOS boundary table in tests/golden/).
+OCP/UOS boundary table in tests/golden/; bf16_bits_to_f64 against
+hand-decoded bit patterns and the sign/exponent/mantissa formula; the
+dual-residual split against its closed-form error bound).
 """
 
 import numpy as np
@@ -188,10 +190,7 @@ def unpack_nibbles(packed, axis=-1):
 
 
 def bf16_bits_to_f64(bits):
-    """Exact value of bfloat16 bit patterns (uint16) as float64."""
+    """Exact value of bfloat16 bit patterns (uint16) as float64: the pattern
+    is the upper half of a float32 whose lower 16 bits are zero."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
-
-
-def f16_bits_to_f64(bits):
-    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)

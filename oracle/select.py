@@ -3,11 +3,11 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: "HyQuant: Hybrid-Precision Quantization for LLM Attention", method
-paragraphs: keys are split into vertical-line positions, a recent sliding
-window and the quantised remainder; the vertical-line score is accumulated
-column mass; the top-rho fraction (5% by default) is taken from the
-non-window prefix; the window size is fixed; identification is a light
-reduction run every 64 tokens.
+paragraphs.  What this module implements from them: each key gets a score,
+the attention probability it has received summed over columns of the
+attention matrix; every few tokens the highest-scoring fraction rho of the
+keys outside a fixed recent window is chosen to stay in full precision,
+together with that window.
 
 Readings
   * Column mass of key t gains, for every recent query r (at most 64, the

@@ -71,6 +71,9 @@ def _prefill(q, k, v, **kw):
     ("neg_scale", mxa.ERR_INVALID_ARG),
     ("out_misaligned", mxa.ERR_INVALID_ARG),
     ("short_row_stride", mxa.ERR_INVALID_ARG),
+    ("k_head_2gib", mxa.ERR_UNSUPPORTED),
+    ("k_scales_2gib", mxa.ERR_UNSUPPORTED),
+    ("v_head_2gib", mxa.ERR_UNSUPPORTED),
 ])
 def test_prefill_rejects(case, status):
     q, k, v = _mx(), _mx(), _mx(layout=1)
@@ -97,9 +100,21 @@ def test_prefill_rejects(case, status):
         kw["out"] = 4100
     elif case == "short_row_stride":
         k.code_stride[2] = 32
+    elif case in ("k_head_2gib", "k_scales_2gib"):
+        # 512K keys in rows of 4 KiB codes (or 4 KiB scales): one K head spans 2 GiB.
+        s = 1 << 19
+        q, k, v = _mx(s=s), _mx(s=s), _mx(s=s, layout=1)
+        for t in (q, k):
+            t.code_stride[:] = [4096 * s, 4096 * s, 4096] if case == "k_head_2gib" else [64 * s, 64 * s, 64]
+            t.scale_stride[:] = [4096 * s, 4096 * s, 4096] if case == "k_scales_2gib" else [4 * s, 4 * s, 4]
+    elif case == "v_head_2gib":
+        # 128 channel rows of 16 MiB: one V head spans 2 GiB.
+        v.code_stride[:] = [128 << 24, 128 << 24, 1 << 24]
     st = _prefill(q, k, v, **kw)
     assert st == status
     assert len(mxa.library().mxattn_last_error()) > 0
+    if case.endswith("2gib"):
+        assert b"2 GiB" in mxa.library().mxattn_last_error()
 
 
 @pytest.mark.parametrize("case, status", [
@@ -406,3 +421,39 @@ def test_decode_unencoded_query_rejects():
     st = lib.mxattn_decode(ctypes.byref(q), ctypes.byref(qr), ctypes.c_void_p(16), ctypes.byref(k), ctypes.byref(k),
                            ctx, None, 0.0, 256, ws, 1 << 20, out, None, None)
     assert st == 2 and b"dual" in lib.mxattn_last_error()
+
+
+@pytest.mark.parametrize("case", ["idx_int64", "idx_shape", "nsel_shape", "ksel_fp16", "ksel_strided",
+                                  "vwin_short", "qbf16_missing"])
+def test_decode_hybrid_arguments_checked_in_binding(case):
+    """The hybrid set reaches the C ABI as bare pointers, so the binding checks
+    dtype, contiguity and shape of every tensor before anything is called
+    (CPU tensors: a check that passed would reach the library and fail there
+    with a different error)."""
+    import torch
+    b, hq, hkv, t, d, w, ms = 2, 8, 2, 256, 128, 16, 12
+    cache = mxa.MX(torch.zeros((b, hkv, t, d // 2), dtype=torch.uint8),
+                   torch.zeros((b, hkv, t, d // 32), dtype=torch.uint8), (b, hkv, t, d), "hd")
+    q = mxa.MX(torch.zeros((b, hq, 1, d // 2), dtype=torch.uint8),
+               torch.zeros((b, hq, 1, d // 32), dtype=torch.uint8), (b, hq, 1, d), "hd")
+    bf = dict(dtype=torch.bfloat16)
+    hy = {"idx": torch.zeros((b, hkv, ms), dtype=torch.int32), "n_sel": torch.zeros((b, hkv), dtype=torch.int32),
+          "k_sel": torch.zeros((b, hkv, ms, d), **bf), "v_sel": torch.zeros((b, hkv, ms, d), **bf),
+          "k_win": torch.zeros((b, hkv, w, d), **bf), "v_win": torch.zeros((b, hkv, w, d), **bf), "window": w}
+    qb = torch.zeros((b, hq, d), **bf)
+    if case == "idx_int64":
+        hy["idx"] = hy["idx"].long()
+    elif case == "idx_shape":
+        hy["idx"] = torch.zeros((b, hq, ms), dtype=torch.int32)
+    elif case == "nsel_shape":
+        hy["n_sel"] = torch.zeros((b,), dtype=torch.int32)
+    elif case == "ksel_fp16":
+        hy["k_sel"] = hy["k_sel"].half()
+    elif case == "ksel_strided":
+        hy["k_sel"] = torch.zeros((b, hkv, d, ms), **bf).transpose(2, 3)
+    elif case == "vwin_short":
+        hy["v_win"] = torch.zeros((b, hkv, w - 1, d), **bf)
+    elif case == "qbf16_missing":
+        qb = None
+    with pytest.raises(ValueError, match="decode hybrid"):
+        mxa.decode(q, cache, cache, torch.full((b,), t, dtype=torch.int32), split_len=128, hybrid=hy, q_bf16=qb)

@@ -351,3 +351,127 @@ def test_hybrid_prefill_weights_normalised():
     assert (w >= 0).all()
     np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-12)
     assert np.all(np.triu(w, 1) == 0)
+
+
+# ---------------------------------------------------------------- two-tile golden
+def _golden_rows(name):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    with open(path) as f:
+        return [ln.split() for ln in (l.strip() for l in f) if ln and not ln.startswith("#")]
+
+
+def _two_tile_case(case):
+    """The inputs of tests/golden/two_tile_running_max.txt (see its header)."""
+    if case in ("A", "B"):
+        logit = np.zeros(34)
+        logit[32] = np.log(0.3 if case == "A" else 0.46875)
+        logit[33] = np.log(0.2)
+        ia, ib = 32, 33
+    else:
+        logit = np.full(64, -60.0)
+        logit[0], logit[1] = np.log(0.3), np.log(0.2)
+        logit[32:] = 0.0
+        ia, ib = 0, 1
+    k = np.stack([logit, np.zeros_like(logit)], axis=1)
+    v = np.zeros_like(k)
+    v[ia, 0] = 1.0
+    v[ib, 1] = 1.0
+    return np.array([[1.0, 0.0]]), k, v
+
+
+@pytest.mark.parametrize("row", _golden_rows("two_tile_running_max.txt"), ids=" ".join)
+def test_two_tile_running_max_golden(row):
+    """Hand-worked two-tile rows: the exponentials of a tile are quantised
+    against the running maximum after that tile (not the tile's own maximum,
+    not the row's final one), earlier tiles are rescaled, and l follows the
+    chosen rule (HiFA4, Abstract; MXAttention, Abstract)."""
+    case, rule, lmode = row[:3]
+    w_a, w_b, lval = (float(x) for x in row[3:])
+    q, k, v = _two_tile_case(case)
+    res = attention.prefill_head(q, k, v, softmax_scale=1.0, kv_tile=32,
+                                 p_rule=mx.RULE_OCP if rule == "ocp" else mx.RULE_UOS,
+                                 l_from_quantized=(lmode == "pnq"))
+    np.testing.assert_allclose(res["l"], [lval], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["out"][0], [w_a / lval, w_b / lval], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], [np.log(lval)], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["m"], [0.0], atol=0)
+
+
+# ---------------------------------------------------------------- GQA wrappers
+def _gqa_inputs(seed, b=2, hq=6, hkv=2, s=70, d=64):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((b, hq, s, d)), rng.standard_normal((b, hkv, s, d)),
+            rng.standard_normal((b, hkv, s, d)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_multihead_prefill_gqa_equals_repeated_kv(causal):
+    """attention.prefill maps query head g to a KV head; checked against the
+    repeat-each-KV-head-consecutively form of grouped-query attention
+    (np.repeat along the head axis), with textbook softmax when P is not
+    quantised and the direct whole-row PNQ when one tile spans the row."""
+    q, k, v = _gqa_inputs(21)
+    g = q.shape[1] // k.shape[1]
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    sc = 1 / 8
+    out0, lse0, _ = attention.prefill(q, k, v, causal=causal, quantize_p=False)
+    out1, _, bnd = attention.prefill(q, k, v, causal=causal, kv_tile=128, envelope=True)
+    assert out0.shape == q.shape and lse0.shape == q.shape[:3] and bnd.shape == q.shape[:3]
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            np.testing.assert_allclose(out0[b, h], _textbook(q[b, h], kr[b, h], vr[b, h], causal, sc), atol=1e-12)
+            np.testing.assert_allclose(out1[b, h], _direct_pnq(q[b, h], kr[b, h], vr[b, h], causal, sc,
+                                                               mx.RULE_OCP, 7.25), atol=1e-12)
+
+
+def test_multihead_prefill_row_samples():
+    q, k, v = _gqa_inputs(22)
+    rows = {(b, h): np.array([0, 1 + h, 69 - b]) for b in range(2) for h in range(6)}
+    full, _, _ = attention.prefill(q, k, v, causal=True)
+    part, _, _ = attention.prefill(q, k, v, causal=True, rows=rows)
+    for (b, h), r in rows.items():
+        np.testing.assert_allclose(part[b, h], full[b, h, r], atol=0)
+
+
+def test_multihead_decode_gqa_and_hybrid_sets():
+    """attention.decode: each (b, hq) pair against textbook softmax over the
+    KV head repeated per group; the hybrid sets, keyed by (b, KV head), are
+    substituted into the repeated rows the same way."""
+    rng = np.random.default_rng(23)
+    b, hq, hkv, t, d = 2, 8, 2, 300, 64
+    g = hq // hkv
+    q = rng.standard_normal((b, hq, d))
+    k, v = rng.standard_normal((b, hkv, t, d)), rng.standard_normal((b, hkv, t, d))
+    ctx = np.array([300, 123])
+    qb = q + 0.01 * rng.standard_normal(q.shape)
+    sets = {}
+    ks, vs = k.copy(), v.copy()
+    for bb in range(b):
+        for h in range(hkv):
+            toks = np.sort(rng.choice(int(ctx[bb]), size=20, replace=False))
+            kk, vv = rng.standard_normal((20, d)), rng.standard_normal((20, d))
+            sets[(bb, h)] = {"tokens": toks, "k": kk, "v": vv}
+            ks[bb, h, toks], vs[bb, h, toks] = kk, vv
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    ksr, vsr = np.repeat(ks, g, axis=1), np.repeat(vs, g, axis=1)
+    plain = attention.decode(q, k, v, ctx)
+    pairs = [(0, 0), (0, 5), (1, 3), (1, 7)]
+    hyb = attention.decode(q, k, v, ctx, pairs=pairs, hybrid={"sets": sets, "q": qb})
+    assert sorted(plain) == [(bb, h) for bb in range(b) for h in range(hq)] and sorted(hyb) == sorted(pairs)
+    sc = 1 / 8
+    for (bb, h), (o, lse) in plain.items():
+        c = int(ctx[bb])
+        s = sc * (kr[bb, h, :c] @ q[bb, h])
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(o, p @ vr[bb, h, :c] / p.sum(), atol=1e-12)
+        np.testing.assert_allclose(lse, s.max() + np.log(p.sum()), atol=1e-12)
+    for (bb, h), (o, _) in hyb.items():
+        c = int(ctx[bb])
+        toks = sets[(bb, h // g)]["tokens"]
+        s = sc * (kr[bb, h, :c] @ q[bb, h])
+        s[toks] = sc * (ksr[bb, h, toks] @ qb[bb, h])
+        vals = vr[bb, h, :c].copy()
+        vals[toks] = vsr[bb, h, toks]
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(o, p @ vals / p.sum(), atol=1e-12)

@@ -247,3 +247,19 @@ def test_smooth_apply_is_float32_multiply():
     assert y.dtype == np.float32
     assert y[0, 0, 0] == np.float32(np.float32(1.0 + 2 ** -7) * np.float32(1.0 / 3.0))
     assert y[0, 0, 1] == 6.0
+
+
+def test_bf16_bits_decode_hand_values_and_formula():
+    """bf16_bits_to_f64 on hand-decoded patterns, then on every finite
+    pattern against sign * 2^(E-127) * (1 + M/128) (2^-126 * M/128 for E = 0)."""
+    hand = {0x0000: 0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x3FC0: 1.5, 0x4049: 3.140625,
+            0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127, 0xC2F7: -123.5}
+    got = mx.bf16_bits_to_f64(np.array(list(hand), dtype=np.uint16))
+    np.testing.assert_array_equal(got, np.array(list(hand.values())))
+    assert np.signbit(mx.bf16_bits_to_f64(np.uint16(0x8000)))
+    bits = np.concatenate([np.arange(0, 0x7F80), np.arange(0x8000, 0xFF80)]).astype(np.uint16)
+    b = bits.astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    ex, man = (b >> 7) & 0xFF, b & 0x7F
+    want = sign * np.where(ex == 0, np.ldexp(man / 128.0, -126), np.ldexp(1.0 + man / 128.0, ex - 127))
+    np.testing.assert_array_equal(mx.bf16_bits_to_f64(bits), want)
