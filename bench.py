@@ -32,6 +32,14 @@ PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline)"
 
+# Launch configurations the legs time (tests/test_gpu_bench_configs.py runs
+# the same calls against the oracle).
+KV_TILE = 128           # prefill key tile
+DECODE_SPLIT = 4096     # tokens per split, 32K batch-32 decode
+HYBRID_SPLIT = 2752     # tokens per split, 32K batch-8 hybrid decode: 12 splits x 64 (sequence, KV head)
+                        # = 768 workgroups, one round at three per CU
+HYBRID_WINDOW = 128     # bf16 recent window (decode and hybrid prefill)
+
 # HBM bytes per launch of the dominant kernels, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) each scaled by what the same
 # counter reads for an elementwise kernel of known size (--calibrate-copy).
@@ -77,11 +85,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,diffusion,decode,hybrid",
                     help="comma list of legs to run (prefill is the headline)")
-    ap.add_argument("--kv-tile", type=int, default=128)
-    ap.add_argument("--decode-split", type=int, default=4096, help="tokens per split, 32K decode leg")
-    ap.add_argument("--hybrid-split", type=int, default=2752,
-                    help="tokens per split, hybrid decode leg (12 splits x 64 (sequence, KV head) = 768 workgroups: "
-                         "one round at three per CU)")
+    ap.add_argument("--kv-tile", type=int, default=KV_TILE)
+    ap.add_argument("--decode-split", type=int, default=DECODE_SPLIT, help="tokens per split, 32K decode leg")
+    ap.add_argument("--hybrid-split", type=int, default=HYBRID_SPLIT, help="tokens per split, hybrid decode leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run an elementwise kernel of known size (1 GiB in, 1 GiB out) three times, "
                          "to scale HBM byte counters; prints the source digests of the profiled kernels")
@@ -155,10 +161,12 @@ def prefill_leg(args):
     # Hybrid prefill: the top 5% vertical-line keys by column mass of the last
     # 64 queries, and a 128-key window per row, in bf16 (selection untimed
     # here, timed on its own).
-    W = 128
+    W = HYBRID_WINDOW
     ctx = torch.tensor([S], dtype=torch.int32, device="cuda")
     col = torch.zeros((B, HKV, S), dtype=torch.float32, device="cuda")
-    qr = mxa.quantize(d["q"][:, :, S - 64:], "hd")
+    # The last 64 queries with the same Smooth-QK factor as Q, against the
+    # smoothed K the step wrote: their logits are those of the attention.
+    qr = mxa.quantize(d["q"][:, :, S - 64:], "hd", chan_scale=qs)
     step()
     sel_ws = torch.empty(mxa.select_workspace_bytes(B, HQ, 64, S), dtype=torch.uint8, device="cuda")
 
@@ -377,7 +385,7 @@ def hybrid_leg(args, flush):
     import bit_microscaled_flashattention_amd as mxa
     import synth
 
-    B, HQ, HKV, T, D, W = 8, 32, 8, 32768, 128, 128
+    B, HQ, HKV, T, D, W = 8, 32, 8, 32768, 128, HYBRID_WINDOW
     SPLIT = args.hybrid_split
     d = synth.hybrid_decode(device="cuda")
     kc, vc = mxa.quantize(d["k"], "hd"), mxa.quantize(d["v"], "hd")

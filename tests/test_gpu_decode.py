@@ -12,7 +12,8 @@ import torch
 import bit_microscaled_flashattention_amd as mxa
 import synth
 from oracle import attention, mx, rotate, select
-from tests.helpers import assert_codes_equal, head_slice, host_f64, oracle_dequant, oracle_quantize
+from tests.helpers import (assert_codes_equal, check_selection, head_slice, host_f64, oracle_dequant,
+                           oracle_quantize)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -449,21 +450,6 @@ def test_topk_exact_on_edge_masses(kind):
             assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
 
 
-def _check_selection(gpu_idx, gpu_n, oracle_cm, ctx, window, num, den, what):
-    k, nn = select.n_select(ctx, window, num, den)
-    assert gpu_n == k, f"{what}: count {gpu_n} vs {k}"
-    cm = oracle_cm[:nn]
-    order = np.sort(cm)[::-1]
-    tau = order[k - 1]
-    eps = 1e-4 * max(order[0], 1e-30)
-    got = set(gpu_idx.tolist())
-    assert len(got) == k and all(0 <= t < nn for t in got)
-    assert np.all(np.diff(gpu_idx) > 0), "indices must be ascending"
-    sure_in = set(np.nonzero(cm > tau + eps)[0].tolist())
-    assert sure_in <= got, f"{what}: {len(sure_in - got)} clearly heavier tokens missing"
-    assert all(cm[t] >= tau - eps for t in got), f"{what}: a clearly lighter token was selected"
-
-
 def test_select_vertical_32k_batch8():
     """col_mass from 64 recent queries x 4 heads per KV head over ctx 32768,
     then the top 5% of the non-window prefix; two calls accumulate."""
@@ -485,7 +471,7 @@ def test_select_vertical_32k_batch8():
         ocm = select.colmass_update(np.zeros(32768), qd, kd, 32768)
         np.testing.assert_allclose(col1[b, h].cpu().numpy(), ocm, rtol=2e-4, atol=1e-7)
         np.testing.assert_allclose(col[b, h].cpu().numpy(), 2 * ocm, rtol=2e-4, atol=2e-7)
-        _check_selection(idx[b, h, : int(n[b, h])].cpu().numpy(), int(n[b, h]), ocm, 32768, 128, 5, 100,
+        check_selection(idx[b, h, : int(n[b, h])].cpu().numpy(), int(n[b, h]), ocm, 32768, 128, 5, 100,
                          f"select b{b} h{h}")
         # The mass actually concentrates on few keys (vertical lines).
         top = np.sort(ocm[:32640])[::-1]

@@ -10,8 +10,8 @@ import torch
 import bit_microscaled_flashattention_amd as mxa
 import synth
 from oracle import attention, mx, rotate, smooth
-from tests.helpers import (assert_codes_equal, check_within, head_slice, host_f64,
-                           oracle_dequant, oracle_quantize)
+from tests.helpers import (assert_codes_equal, check_prefill, head_slice, host_f64, oracle_dequant,
+                           oracle_quantize)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -38,58 +38,9 @@ def _run_case(q, k, v, *, causal, kv_tile=128, p_rule="ocp", qkv_rule="ocp", l_f
                                       hybrid.get("n_sel"), kv_tile=kv_tile, p_rule=p_rule,
                                       l_from_quantized=l_from_quantized, out_dtype=out_dtype, return_lse=True)
     torch.cuda.synchronize()
-    bsz, hq, _, _ = q.shape
-    hkv = k.shape[1]
-    grp = hq // hkv
-    heads = list(range(hq)) if heads is None else list(heads)
-    kv_heads = sorted({h // grp for h in heads})
-    r = mx.RULE_OCP if qkv_rule == "ocp" else mx.RULE_UOS
-    pr = mx.RULE_OCP if p_rule == "ocp" else mx.RULE_UOS
-    qsel = torch.as_tensor(heads, device=q.device)
-    ksel = torch.as_tensor(kv_heads, device=q.device)
-    q32 = host_f64(q.index_select(1, qsel)).astype(np.float32)
-    k32 = host_f64(k.index_select(1, ksel)).astype(np.float32)
-    if q_scale is not None:
-        q32 = smooth.apply(q32, q_scale.cpu().numpy()[heads])
-        k32 = smooth.apply(k32, k_scale.cpu().numpy()[kv_heads])
-    if hadamard:
-        q32 = rotate.hadamard_f32(q32, axis=3)
-        k32 = rotate.hadamard_f32(k32, axis=3)
-    oq = oracle_quantize(q32.astype(np.float64), "hd", r)
-    ok = oracle_quantize(k32.astype(np.float64), "hd", r)
-    ov = oracle_quantize(host_f64(v.index_select(1, ksel)), "key", r)
-    assert_codes_equal(head_slice(qh, heads), *oq, what + " q")
-    assert_codes_equal(head_slice(kh, kv_heads), *ok, what + " k")
-    assert_codes_equal(head_slice(vh, kv_heads), *ov, what + " v")
-    qd = oracle_dequant(*oq, "hd")
-    kd = oracle_dequant(*ok, "hd")
-    vd = oracle_dequant(*ov, "key", n=v.shape[2])
-    got = out.float().cpu().numpy()
-    glse = lse.cpu().numpy()
-    atol = ATOL if out_dtype == torch.float32 else ATOL + 8e-3
-    worst, n_env = 0.0, 0
-    for bi in range(bsz):
-        for i, h in enumerate(heads):
-            kvi = kv_heads.index(h // grp)
-            rr = None if rows is None else rows[h]
-            hy = None
-            if hybrid is not None:
-                kvh = h // grp
-                sel = np.zeros(0, dtype=np.int64)
-                if hybrid.get("idx") is not None:
-                    sel = hybrid["idx"][bi, kvh, :int(hybrid["n_sel"][bi, kvh])].cpu().numpy()
-                hy = {"window": hybrid["window"], "sel": sel, "q": host_f64(q[bi, h]),
-                      "k": host_f64(k[bi, kvh]), "v": host_f64(v[bi, kvh])}
-            res = attention.prefill_head(qd[bi, i], kd[bi, kvi], vd[bi, kvi], causal=causal,
-                                         kv_tile=kv_tile, p_rule=pr, l_from_quantized=l_from_quantized,
-                                         rows=rr, envelope=True, hybrid=hy)
-            g_rows = got[bi, h] if rr is None else got[bi, h][rr]
-            l_rows = glse[bi, h] if rr is None else glse[bi, h][rr]
-            worst = max(worst, check_within(g_rows, res["out"], res["bound"], atol, f"{what} b{bi} h{h}"))
-            n_env += int((res["bound"] > 0).sum())
-            np.testing.assert_allclose(l_rows, res["lse"], atol=1e-3, rtol=0)
-    print(f"  worst |err| {worst:.3e}; rows needing the envelope: {n_env}", flush=True)
-    return worst
+    return check_prefill(q, k, v, qh, kh, vh, out, lse, causal=causal, kv_tile=kv_tile, p_rule=p_rule,
+                         qkv_rule=qkv_rule, l_from_quantized=l_from_quantized, rows=rows, q_scale=q_scale,
+                         k_scale=k_scale, heads=heads, what=what, hadamard=hadamard, hybrid=hybrid)
 
 
 def test_tiny_noncausal_128x64():
@@ -332,27 +283,6 @@ def test_hybrid_prefill_limits():
     torch.cuda.synchronize()
     assert torch.equal(plain, hy0) and torch.equal(lp, l0)
     _run_case(q, k, v, causal=True, hybrid={"window": 300}, what="hybrid all-bf16 window")
-
-
-def test_hybrid_prefill_4k_gqa_selected_by_column_mass():
-    """The 4K causal GQA workload with the selection the decode side uses:
-    column mass of the last 64 queries over the non-window prefix, top 5%,
-    window 128; sampled rows of four heads against the oracle."""
-    d = synth.gqa_prefill(device=DEV)
-    S, W = 4096, 128
-    qh_recent = mxa.quantize(d["q"][:, :, S - 64:], "hd")
-    kh = mxa.quantize(d["k"], "hd")
-    ctx = torch.tensor([S], dtype=torch.int32, device=DEV)
-    col = torch.zeros((1, 8, S), dtype=torch.float32, device=DEV)
-    idx, n = mxa.select_vertical(qh_recent, kh, ctx, col, window=W)
-    torch.cuda.synchronize()
-    print(f"selected per KV head: {n.cpu().numpy().ravel().tolist()}", flush=True)
-    rng = np.random.default_rng(5)
-    heads = [0, 11, 22, 31]
-    rows = {h: np.unique(np.concatenate([[0, 1, 127, 128, 129, 4095], rng.integers(0, S, 40)])) for h in heads}
-    _run_case(d["q"], d["k"], d["v"], causal=True, heads=heads, rows=rows,
-              hybrid={"window": W, "idx": idx.contiguous(), "n_sel": n.contiguous()},
-              what="hybrid 4k gqa")
 
 
 def test_hybrid_prefill_cuts_error_on_heavy_columns():
