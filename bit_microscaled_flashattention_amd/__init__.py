@@ -102,6 +102,7 @@ def _load():
         "mxattn_decode": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, sz, vp, vp, vp],
         "mxattn_decode_paged": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), P(_Paging), vp, P(_Hybrid), f32, i32, vp, sz,
                                 vp, vp, vp],
+        "mxattn_decode_noalloc": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, vp, vp],
         "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, i32, P(_Mx), P(_Mx), vp],
         "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
     }
@@ -127,7 +128,7 @@ _lib = _load()
 EXPORTS = (
     "mxattn_quantize", "mxattn_quantize_dual", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
     "mxattn_prefill_hybrid",
-    "mxattn_decode_workspace_bytes", "mxattn_decode", "mxattn_decode_paged",
+    "mxattn_decode_workspace_bytes", "mxattn_decode", "mxattn_decode_paged", "mxattn_decode_noalloc",
     "mxattn_select_workspace_bytes", "mxattn_select_vertical",
     "mxattn_status_string", "mxattn_last_error", "mxattn_version",
 )
@@ -383,8 +384,23 @@ def _check_hybrid(hy, q_bf16, b, hq, hkv, d):
          f"q_bf16 must be contiguous bfloat16 [{b},{hq},{d}]")
 
 
+DECODE_SCRATCH_BYTES = 16 << 20   # the built-in scratch of decode_noalloc
+
+
+def decode_noalloc(q, k_cache, v_cache, ctx_len, out, softmax_scale=0.0, split_len=2048, hybrid=None,
+                   q_bf16=None, lse=None, q_res=None):
+    """decode() through mxattn_decode_noalloc: no workspace, no allocation by
+    the library or by this wrapper (out [B,Hq,D] fp32 and the optional lse
+    [B,Hq] fp32 are the caller's).  The partial slots use the library's
+    per-device scratch, so calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("decode_noalloc: out must be given (the call allocates nothing)")
+    return _decode(q, k_cache, v_cache, None, k_cache.shape[2], ctx_len, softmax_scale, split_len, hybrid,
+                   q_bf16, None, lse is not None, out, q_res, noalloc=True, lse=lse)
+
+
 def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, q_bf16, workspace, return_lse,
-            out, q_res):
+            out, q_res, noalloc=False, lse=None):
     if isinstance(q, torch.Tensor):
         # bf16 query [B,Hq,D] or [B,Hq,1,D]: the scan encodes it (OCP), no
         # separate quantiser launch.
@@ -399,12 +415,17 @@ def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, 
     if hybrid is not None:
         _check_hybrid(hybrid, q_bf16, b, hq, hkv, d)
     hy_rows = (hybrid["idx"].shape[-1] + int(hybrid["window"])) if hybrid is not None else 0
-    need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hy_rows)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not noalloc:
+        need = decode_workspace_bytes(b, hq, hkv, d, tcap, split_len, hy_rows)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty((b, hq, d), dtype=torch.float32, device=dev)
-    lse = torch.empty((b, hq), dtype=torch.float32, device=dev) if return_lse else None
+    if return_lse and lse is None:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=dev)
+    for t, shape in ((out, (b, hq, d)), (lse, (b, hq))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != math.prod(shape)):
+            raise ValueError(f"decode: out/lse must be contiguous float32 {shape}")
     hy = None
     if hybrid is not None:
         hy = _Hybrid()
@@ -417,7 +438,12 @@ def _decode(q, kc, vc, paging, tcap, ctx_len, softmax_scale, split_len, hybrid, 
     dq, dk, dv = q.desc(), kc.desc(), vc.desc()
     dqr = q_res.desc() if q_res is not None else None
     common = (ctypes.byref(dqr) if dqr is not None else None, _ptr(q_bf16), ctypes.byref(dk), ctypes.byref(dv))
-    tail = (_ptr(ctx_len), ctypes.byref(hy) if hy is not None else None, float(softmax_scale), int(split_len),
+    hyp = ctypes.byref(hy) if hy is not None else None
+    if noalloc:
+        _check(_lib.mxattn_decode_noalloc(ctypes.byref(dq), *common, _ptr(ctx_len), hyp, float(softmax_scale),
+                                          int(split_len), _ptr(out), _ptr(lse), _stream(kc.codes)))
+        return (out, lse) if return_lse else out
+    tail = (_ptr(ctx_len), hyp, float(softmax_scale), int(split_len),
             _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(kc.codes))
     if paging is None:
         _check(_lib.mxattn_decode(ctypes.byref(dq), *common, *tail))

@@ -22,6 +22,7 @@
 #include "kernels.h"
 
 static_assert(MXATTN_MAX_QUANTIZE_JOBS == mxattn::kMaxQuantJobs, "batch size limits differ");
+static_assert(MXATTN_DECODE_SCRATCH_BYTES == mxattn::kDecodeScratchBytes, "decode scratch sizes differ");
 
 using namespace mxattn;
 
@@ -403,7 +404,7 @@ static mxattn_status_t decode_common(const mxattn_mx_t* q, const mxattn_mx_t* q_
                                      const mxattn_mx_t* kc, const mxattn_mx_t* vc, const mxattn_paging_t* pg,
                                      const int32_t* ctx_len, const mxattn_hybrid_t* hy, float softmax_scale,
                                      int32_t split_len, void* workspace, size_t workspace_bytes, float* out,
-                                     float* lse, mxattn_stream_t stream) {
+                                     float* lse, mxattn_stream_t stream, bool use_scratch = false) {
   mxattn_status_t st;
   // A query descriptor without codes and scales gives only the shape: the
   // scan encodes q_bf16 itself.
@@ -475,6 +476,15 @@ static mxattn_status_t decode_common(const mxattn_mx_t* q, const mxattn_mx_t* q_
     return fail(MXATTN_ERR_UNSUPPORTED, "decode: problem too large for one launch");
   const size_t need = mxattn_decode_workspace_bytes(q->batch, q->heads, kc->heads, q->dim, tcap, split_len,
                                                     static_cast<int32_t>(hybrid_rows));
+  if (use_scratch) {
+    // The built-in scratch: sized once, looked up (not allocated) per device.
+    if (need > kDecodeScratchBytes)
+      return fail(MXATTN_ERR_UNSUPPORTED, "decode_noalloc: %zu bytes of partial slots needed, the built-in scratch "
+                  "holds %zu; use mxattn_decode with a workspace or a longer split_len", need, kDecodeScratchBytes);
+    const hipError_t e = decode_scratch(&workspace);
+    if (e != hipSuccess) return fail(MXATTN_ERR_HIP, "decode_noalloc: scratch address: %s", hipGetErrorString(e));
+    workspace_bytes = kDecodeScratchBytes;
+  }
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MXATTN_ERR_WORKSPACE, "decode: workspace of %zu bytes needed", need);
   if (!aligned16(workspace)) return fail(MXATTN_ERR_INVALID_ARG, "decode: workspace not 16-byte aligned");
@@ -530,6 +540,16 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
   if (injected("decode", &st)) return st;
   return decode_common(q, q_res, q_bf16, kc, vc, nullptr, ctx_len, hy, softmax_scale, split_len, workspace,
                        workspace_bytes, out, lse, stream);
+}
+
+mxattn_status_t mxattn_decode_noalloc(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,
+                                      const mxattn_mx_t* kc, const mxattn_mx_t* vc, const int32_t* ctx_len,
+                                      const mxattn_hybrid_t* hy, float softmax_scale, int32_t split_len, float* out,
+                                      float* lse, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("decode_noalloc", &st)) return st;
+  return decode_common(q, q_res, q_bf16, kc, vc, nullptr, ctx_len, hy, softmax_scale, split_len, nullptr, 0, out,
+                       lse, stream, true);
 }
 
 mxattn_status_t mxattn_decode_paged(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,

@@ -21,6 +21,8 @@
 //   * The next chunks' K and V bytes are loaded (non-temporal: the cache is
 //     streamed once) while the current one is computed.  Partial (O, m, l) per split go to the workspace and a merge
 //     kernel combines them in a fixed order (deterministic).
+#include <mutex>
+
 #include "mx_device.h"
 #include "kernels.h"
 
@@ -628,6 +630,34 @@ static void launch_scan(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((decode_scan_kernel<D, DUAL, true>), grid, dim3(kDecThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_scan_kernel<D, DUAL, false>), grid, dim3(kDecThreads), 0, stream, a);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of mxattn_decode_noalloc: the partial slots in a file-scope device
+// array instead of a caller's workspace, for callers that cannot allocate.
+// Every device the library runs on holds its own copy until the process
+// ends.  In host code the array's name is only a stand-in: its address on the
+// current device comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream) {

@@ -151,6 +151,12 @@ hipError_t launch_quantize_batch(const QuantArgs* jobs, int n, hipStream_t strea
 hipError_t launch_smooth_calibrate(const CalibArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int D, hipStream_t stream);
+
+// Built-in partial-slot scratch of mxattn_decode_noalloc (one copy per device).
+constexpr size_t kDecodeScratchBytes = size_t{16} << 20;
+// Device address of that scratch on the current device (looked up once per
+// device, then cached).
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream);
 
 }  // namespace mxattn

@@ -299,6 +299,30 @@ mxattn_status_t mxattn_decode(const mxattn_mx_t* q, const mxattn_mx_t* q_res, co
                               float* out, float* lse, mxattn_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * mxattn_decode_noalloc -- mxattn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The partial slots
+ * live in a library-owned device array of 16 MiB (MXATTN_DECODE_SCRATCH_BYTES)
+ * that each GPU holds, once the library has run on it, until the process
+ * ends; the call allocates and frees nothing.  Every argument and the result
+ * are those of mxattn_decode (same kernels, the same bits).
+ *   A problem whose mxattn_decode_workspace_bytes exceeds the scratch is
+ *   refused with MXATTN_ERR_UNSUPPORTED before anything runs (a longer
+ *   split_len needs fewer slots).
+ *   The first call on a device looks up the array's device address
+ *   (MXATTN_ERR_HIP if that fails).
+ *   All calls on one GPU share its array and it keeps the last call's
+ *   contents: calls that may overlap on one GPU (different streams, or
+ *   several host threads) race and must be serialised by the caller. */
+#define MXATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+mxattn_status_t mxattn_decode_noalloc(const mxattn_mx_t* q, const mxattn_mx_t* q_res, const void* q_bf16,
+                                      const mxattn_mx_t* k_cache, const mxattn_mx_t* v_cache,
+                                      const int32_t* ctx_len, const mxattn_hybrid_t* hybrid,
+                                      float softmax_scale, int32_t split_len, float* out, float* lse,
+                                      mxattn_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * mxattn_decode_paged -- mxattn_decode over a paged MXFP4 KV cache
  * (BitDecoding-FP4, "System-Level Optimization": the cache is split into
  * fixed-size pages placed anywhere in GPU memory and found through a block

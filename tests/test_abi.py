@@ -457,3 +457,46 @@ def test_decode_hybrid_arguments_checked_in_binding(case):
         qb = None
     with pytest.raises(ValueError, match="decode hybrid"):
         mxa.decode(q, cache, cache, torch.full((b,), t, dtype=torch.int32), split_len=128, hybrid=hy, q_bf16=qb)
+
+
+def test_decode_noalloc_refuses_problems_beyond_its_scratch():
+    """The no-allocation decode checks that its partial slots fit the 16 MiB
+    built-in scratch before it touches the device (here there is none: a
+    check that passed would fail later with a different status)."""
+    lib = mxa.library()
+    b, hq, hkv, t = 64, 64, 16, 32768
+    q, k = _mx(b=b, h=hq, s=1), _mx(b=b, h=hkv, s=t)
+    need = lib.mxattn_decode_workspace_bytes(b, hq, hkv, 128, t, 2048, 0)
+    assert need > mxa.DECODE_SCRATCH_BYTES
+    st = lib.mxattn_decode_noalloc(ctypes.byref(q), None, None, ctypes.byref(k), ctypes.byref(k),
+                                   ctypes.c_void_p(64), None, 0.0, 2048, ctypes.c_void_p(4096), None, None)
+    assert st == mxa.ERR_UNSUPPORTED
+    assert b"scratch" in lib.mxattn_last_error()
+    # Argument errors come first, as for mxattn_decode.
+    q.codes = None
+    st = lib.mxattn_decode_noalloc(ctypes.byref(q), None, None, ctypes.byref(k), ctypes.byref(k),
+                                   ctypes.c_void_p(64), None, 0.0, 2048, ctypes.c_void_p(4096), None, None)
+    assert st == mxa.ERR_INVALID_ARG
+
+
+def test_decode_noalloc_python_wrapper_needs_out():
+    with pytest.raises(ValueError, match="out must be given"):
+        mxa.decode_noalloc(None, None, None, None, None)
+
+
+@pytest.mark.parametrize("bad", ["out_fp16", "out_shape", "lse_shape"])
+def test_decode_output_checked_in_binding(bad):
+    """out [B,Hq,D] and lse [B,Hq] must be contiguous float32 of those sizes;
+    checked before the library is called (CPU tensors)."""
+    import torch
+    b, hq, hkv, t, d = 2, 8, 2, 256, 128
+    cache = mxa.MX(torch.zeros((b, hkv, t, d // 2), dtype=torch.uint8),
+                   torch.zeros((b, hkv, t, d // 32), dtype=torch.uint8), (b, hkv, t, d), "hd")
+    q = mxa.MX(torch.zeros((b, hq, 1, d // 2), dtype=torch.uint8),
+               torch.zeros((b, hq, 1, d // 32), dtype=torch.uint8), (b, hq, 1, d), "hd")
+    out = torch.zeros((b, hq, d), dtype=torch.float16 if bad == "out_fp16" else torch.float32)
+    if bad == "out_shape":
+        out = torch.zeros((b, hq, d - 1))
+    lse = torch.zeros((b, hq + (bad == "lse_shape")))
+    with pytest.raises(ValueError, match="out/lse"):
+        mxa.decode_noalloc(q, cache, cache, torch.full((b,), t, dtype=torch.int32), out, split_len=128, lse=lse)
