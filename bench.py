@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,diffusion,decode,hybrid",
+    ap.add_argument("--legs", default="prefill,diffusion,decode,hybrid,tiny",
                     help="comma list of legs to run (prefill is the headline)")
     ap.add_argument("--kv-tile", type=int, default=KV_TILE)
     ap.add_argument("--decode-split", type=int, default=DECODE_SPLIT, help="tokens per split, 32K decode leg")
@@ -122,6 +122,23 @@ def timed(fn, steps, warmup, kernel_fn=None):
     return wall, kern
 
 
+def launch_events(kernel_fn, n):
+    """Durations of n launches of kernel_fn, each between its own two events
+    on the launch stream, all enqueued before one synchronise so the queue
+    runs ahead of the GPU.  Returns (mean, median) in seconds."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    kernel_fn()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        kernel_fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+    return sum(ts) / n, ts[n // 2]
+
+
 # ------------------------------------------------------------------ prefill
 def prefill_leg(args):
     import torch
@@ -155,7 +172,15 @@ def prefill_leg(args):
         mxa.quantize_batch(rot_jobs)
         attn()
 
-    wall, kern = timed(step, args.steps, args.warmup, attn)
+    wall, kern_b2b = timed(step, args.steps, args.warmup, attn)
+    kern, kern_med = launch_events(attn, args.steps)
+    # The same kernel writing bf16 outputs (half the output bytes).
+    out_bf = torch.empty((B, HQ, S, D), dtype=torch.bfloat16, device="cuda")
+
+    def attn_bf():
+        mxa.prefill(qh, kh, vh, causal=True, kv_tile=args.kv_tile, out=out_bf)
+
+    kern_bf, kern_bf_med = launch_events(attn_bf, args.steps)
     _, quant = timed(lambda: None, args.steps, 0, lambda: mxa.quantize_batch(qkv_jobs))
     wall_r, quant_r = timed(step_rot, args.steps, args.warmup, lambda: mxa.quantize_batch(rot_jobs))
     # Hybrid prefill: the top 5% vertical-line keys by column mass of the last
@@ -188,9 +213,13 @@ def prefill_leg(args):
     pairs = B * HQ * S * (S + 1) // 2
     flops = 4 * D * pairs
     res = {
-        "flops": flops, "step_s": wall, "kernel_s": kern,
+        "flops": flops, "step_s": wall, "kernel_s": kern, "kernel_median_s": kern_med, "kernel_b2b_s": kern_b2b,
         "step_tflops": flops / wall / 1e12, "kernel_tflops": flops / kern / 1e12,
         "quantize_s": quant,
+        "bf16_out": {"kernel_ms": round(kern_bf * 1e3, 4), "kernel_median_ms": round(kern_bf_med * 1e3, 4),
+                     "kernel_tflops": round(flops / kern_bf / 1e12, 2),
+                     "frac": round(flops / kern_bf / 1e12 / PEAK_FP4_TFLOPS, 4),
+                     "note": "the same attention kernel writing bf16 instead of fp32 outputs"},
         "hybrid_prefill": {"ms_per_step": round(wall_h * 1e3, 4), "kernel_ms": round(kern_h * 1e3, 4),
                            "kernel_tflops": round(flops / kern_h / 1e12, 2),
                            "selection_ms": round(sel_t * 1e3, 4),
@@ -206,25 +235,47 @@ def prefill_leg(args):
     return res, d, (qs, ks)
 
 
-def prefill_cpu_baseline(d, cal):
-    """The oracle on 11 of the 32 query heads (every third head), every row:
-    quantisation of those heads' Q, K, V plus the tiled prefill.
-    Rate scaled to the full workload by the fraction of query-key pairs."""
-    import numpy as np
-    import torch
-    from oracle import attention, mx, smooth
-
+# ------------------------------------------------------------------ oracle timings
+# The CPU oracle as it stands (float64 numpy, oracle/), timed on this host on a
+# bounded seeded sample of each workload and scaled to the full one.  Query
+# rows are independent, so the cost of a workload is a per-row part times its
+# rows plus a per-head (or per KV head) part times its heads; both parts are
+# measured and both the measured and the scaled seconds are reported.
+def host_cores():
+    """Threads the oracle may use: BLAS threads (numpy matmul); the
+    elementwise numpy work is single-threaded.  Also the host's counts."""
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = os.cpu_count() or 1
+        blas = os.cpu_count() or 1
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return int(blas), {"os_cpu_count": os.cpu_count(), "affinity": aff, "blas_threads": int(blas)}
+
+
+def _host(t):
+    import torch
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def prefill_cpu_baseline(d, cal):
+    """The oracle on 11 of the 32 query heads (every third head), every row:
+    quantisation of those heads' Q, K, V plus the tiled prefill.  Rate scaled
+    to the full workload by the fraction of query-key pairs.  The same run
+    records the per-tile mass change of P quantisation (HiFA4's tile
+    diagnostic): eps = sum P_hat / sum P_tilde - 1 per (query row, 128-key
+    tile)."""
+    import numpy as np
+    from oracle import attention, mx, smooth
+
+    cores, info = host_cores()
     qs, ks = (c.cpu().numpy() for c in cal)
     heads = list(range(0, 32, 3))
-    q = d["q"][:, heads].float().cpu().numpy()
-    k = d["k"].float().cpu().numpy()
-    v = d["v"].to(torch.float64).cpu().numpy()
+    q = _host(d["q"][:, heads]).astype(np.float32)
+    k = _host(d["k"]).astype(np.float32)
+    v = _host(d["v"])
     S, D = q.shape[2], q.shape[3]
+    eps = []
     t0 = time.perf_counter()
     pairs = 0
     for i, h in enumerate(heads):
@@ -234,16 +285,133 @@ def prefill_cpu_baseline(d, cal):
         qc, qsb = mx.quantize(q32, axis=3)
         kc, ksb = mx.quantize(k32, axis=3)
         vc, vsb = mx.quantize(v[:, kv:kv + 1], axis=2)
-        attention.prefill_head(mx.dequantize(qc, qsb, 3)[0, 0], mx.dequantize(kc, ksb, 3)[0, 0],
-                               mx.dequantize(vc, vsb, 2)[0, 0], causal=True, kv_tile=128)
+        res = attention.prefill_head(mx.dequantize(qc, qsb, 3)[0, 0], mx.dequantize(kc, ksb, 3)[0, 0],
+                                     mx.dequantize(vc, vsb, 2)[0, 0], causal=True, kv_tile=KV_TILE,
+                                     return_tile_eps=True)
+        e = res["tile_eps"]
+        eps.append(e[np.isfinite(e)])
         pairs += S * (S + 1) // 2
     dt = time.perf_counter() - t0
-    return {"value": 4 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{len(heads)} of 32 query heads, all 4096 rows (quantise + tiled PNQ prefill, float64 numpy; "
-                      f"{dt:.1f} s; BLAS threads {blas_threads}, elementwise single-threaded); "
-                      f"rate scaled by pair count to the full workload",
-            "seconds": dt}
+    eps = np.concatenate(eps)
+    out = {"value": 4 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"{len(heads)} of 32 query heads, all 4096 rows (quantise + tiled PNQ prefill, float64 "
+                     f"numpy); {dt:.1f} s measured; rate scaled by pair count to the full workload",
+           "seconds": round(dt, 2), "host": info}
+    tile = {"eps_median": float(np.median(eps)), "eps_mean": float(eps.mean()),
+            "eps_p10": float(np.percentile(eps, 10)), "eps_p90": float(np.percentile(eps, 90)),
+            "tiles": int(eps.size),
+            "note": "per (query row, 128-key tile): sum P_hat / sum P_tilde - 1 under OCP P scales, oracle, "
+                    "the 11 sampled heads of the 4K step"}
+    return out, tile
+
+
+def tiny_cpu_oracle(d):
+    """The whole tiny workload (quantise Q, K, V, one-tile PNQ prefill) on one
+    BLAS thread and on all of them; repeated for at least 1 s each."""
+    import numpy as np
+    from oracle import attention, mx
+    from threadpoolctl import threadpool_limits
+
+    q, k, v = _host(d["q"]), _host(d["k"]), _host(d["v"])
+
+    def run():
+        qc, qsb = mx.quantize(q, axis=3)
+        kc, ksb = mx.quantize(k, axis=3)
+        vc, vsb = mx.quantize(v, axis=2)
+        attention.prefill_head(mx.dequantize(qc, qsb, 3)[0, 0], mx.dequantize(kc, ksb, 3)[0, 0],
+                               mx.dequantize(vc, vsb, 2)[0, 0], causal=False, kv_tile=KV_TILE)
+
+    res = {}
+    cores, info = host_cores()
+    for label, n in (("1_core", 1), ("all_cores", cores)):
+        with threadpool_limits(limits=n):
+            run()
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                run()
+                reps += 1
+                if time.perf_counter() - t0 >= 1.0:
+                    break
+            res[label] = {"ms_per_step": round((time.perf_counter() - t0) / reps * 1e3, 3), "cores": n}
+    res.update(kind="oracle", host=info,
+               sample="the whole workload (1 x 1 x 128 x 64, fp16): quantise Q, K, V + one-tile PNQ prefill")
+    return res
+
+
+def decode_cpu_oracle(k_rows, v_rows, q_rows, n_seq, hq, hkv, tokens, alg_bytes, hybrid_sets=None, q_bf=None):
+    """The oracle's decode step on seeded (sequence, query head) pairs:
+    dequantise the MXFP4 cache rows of each pair's KV head (the cache is
+    stored encoded; encoding it is not part of a step), encode the query,
+    softmax over the context (plus the bf16 set when hybrid).
+
+    k_rows/v_rows: {(b, kv): float64 [T, D] values the cache was encoded
+    from}; q_rows: {(b, h): float64 [D]}.  Scaled as n_seq*hkv KV heads of
+    dequantisation plus n_seq*hq pairs of attention."""
+    import numpy as np
+    from oracle import attention, mx
+
+    cores, info = host_cores()
+    g = hq // hkv
+    cache = {key: (mx.quantize(k_rows[key], axis=1), mx.quantize(v_rows[key], axis=1)) for key in k_rows}
+    t_deq, t_att = 0.0, 0.0
+    for (b, kv), ((kc, ks), (vc, vs)) in cache.items():
+        t0 = time.perf_counter()
+        kd, vd = mx.dequantize(kc, ks, 1), mx.dequantize(vc, vs, 1)
+        t1 = time.perf_counter()
+        for h in range(kv * g, kv * g + g):
+            if (b, h) not in q_rows:
+                continue
+            qc, qsb = mx.quantize(q_rows[(b, h)], axis=0)
+            hy = None
+            if hybrid_sets is not None:
+                toks, kb, vb = hybrid_sets[(b, kv)]
+                hy = {"tokens": toks, "k": kb, "v": vb, "q": q_bf[(b, h)]}
+            attention.decode_head(mx.dequantize(qc, qsb, 0), kd, vd, tokens, hybrid=hy)
+        t_deq += t1 - t0
+        t_att += time.perf_counter() - t1
+    n_kv, n_pairs = len(cache), len(q_rows)
+    full = n_seq * hkv * t_deq / n_kv + n_seq * hq * t_att / n_pairs
+    return {"value": round(full * 1e3, 2), "unit": "ms/token", "GB_per_s": round(alg_bytes / full / 1e9, 3),
+            "cores": cores, "kind": "oracle", "host": info,
+            "sample": f"{n_pairs} seeded (sequence, query head) pairs over {n_kv} KV heads: dequantise their "
+                      f"cache rows, encode the query, {'hybrid ' if hybrid_sets else ''}softmax over {tokens} "
+                      f"tokens; {t_deq + t_att:.2f} s measured, scaled to {n_seq * hkv} KV heads and "
+                      f"{n_seq * hq} pairs",
+            "measured_s": round(t_deq + t_att, 3), "scaled_s": round(full, 2)}
+
+
+def diffusion_cpu_oracle(q, k, v, heads, rows):
+    """The oracle on `rows` seeded query rows of each of `heads` (UOS on Q,
+    K, V and P): encode the head's K and V and the sampled Q rows, tiled PNQ
+    prefill of those rows.  Scaled to 24 heads x 32768 rows."""
+    import numpy as np
+    from oracle import attention, mx
+
+    cores, info = host_cores()
+    R = mx.RULE_UOS
+    t_kv, t_q, t_att = 0.0, 0.0, 0.0
+    S = k.shape[2]
+    for i, h in enumerate(heads):
+        t0 = time.perf_counter()
+        kc, ksb = mx.quantize(k[:, i:i + 1], axis=3, rule=R)
+        vc, vsb = mx.quantize(v[:, i:i + 1], axis=2, rule=R)
+        kd, vd = mx.dequantize(kc, ksb, 3)[0, 0], mx.dequantize(vc, vsb, 2)[0, 0]
+        t1 = time.perf_counter()
+        qc, qsb = mx.quantize(q[:, i:i + 1], axis=3, rule=R)
+        qd = np.zeros((S, q.shape[3]))
+        qd[rows[i]] = mx.dequantize(qc, qsb, 3)[0, 0]
+        t2 = time.perf_counter()
+        attention.prefill_head(qd, kd, vd, causal=False, kv_tile=KV_TILE, p_rule=R, rows=rows[i])
+        t_kv += t1 - t0
+        t_q += t2 - t1
+        t_att += time.perf_counter() - t2
+    n_rows = sum(len(r) for r in rows)
+    full = 24 * t_kv / len(heads) + 24 * S * (t_q + t_att) / n_rows
+    flops = 4 * 128 * 24 * S * S
+    return {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle", "host": info,
+            "sample": f"{len(rows[0])} seeded rows of each of {len(heads)} heads (encode K, V and the rows, tiled "
+                      f"PNQ prefill, UOS); {t_kv + t_q + t_att:.1f} s measured, scaled to 24 heads x {S} rows",
+            "measured_s": round(t_kv + t_q + t_att, 2), "scaled_s": round(full, 1)}
 
 
 # ------------------------------------------------------------------ decode
@@ -283,6 +451,13 @@ def decode_leg(args, flush):
     SPLIT = args.decode_split
     d = synth.long_decode(device="cuda")
     kc, vc = mxa.quantize(d["k"], "hd"), mxa.quantize(d["v"], "hd")
+    # Host copies for the oracle's timing sample: four seeded (sequence, query
+    # head) pairs over two KV heads.
+    picks = [(5, 1), (26, 6)]
+    cpu_pairs = [(5, 4), (5, 6), (26, 25), (26, 27)]
+    k_rows = {key: _host(d["k"][key]) for key in picks} if args.cpu else None
+    v_rows = {key: _host(d["v"][key]) for key in picks} if args.cpu else None
+    q_rows = {key: _host(d["q"][key]) for key in cpu_pairs} if args.cpu else None
     del d["k"], d["v"]
     torch.cuda.empty_cache()
     qh = mxa.empty_mx((B, HQ, 1, D), "hd")
@@ -350,6 +525,7 @@ def decode_leg(args, flush):
     q_mx_bytes = B * HQ * (D // 2 + D // 32)
     alg = cache_bytes + q_bytes + B * HQ * D * 4
     alg_d = cache_bytes + 2 * q_mx_bytes + B * HQ * D * 4
+    cpu = decode_cpu_oracle(k_rows, v_rows, q_rows, B, HQ, HKV, T, alg) if args.cpu else None
     return {
         "workload": "batch 32, 32/8 heads, head_dim 128, ctx 32768, MXFP4 K/V cache (E2M1 + E8M0 per 32 "
                     f"along head_dim), MXFP4 query, split {SPLIT}; step = one decode call (the scan encodes the "
@@ -371,6 +547,7 @@ def decode_leg(args, flush):
             "frac": round(alg_d / t_call_d / 1e9 / PEAK_HBM_GBS, 4),
             "note": "q split into MXFP4(q) + MXFP4(q - dequant(MXFP4(q))); step = quantise both halves + decode",
         },
+        "cpu_oracle": cpu,
         "paged_kv": {
             "call_ms": round(t_call_p * 1e3, 4),
             "achieved_GB_per_s": round(alg / t_call_p / 1e9, 1),
@@ -397,6 +574,9 @@ def hybrid_leg(args, flush):
         return mxa.select_vertical(qr, kc, d["ctx_len"], col, window=W, workspace=sel_ws)
 
     idx, n = select()
+    cpu = None
+    if args.cpu:
+        cpu = hybrid_cpu_oracle(d, [(1, 2), (6, 5)], [(1, 8), (1, 11), (6, 20), (6, 22)], T, W)
     # Gather the bf16 rows of the selected tokens and of the window (caller side).
     max_sel = idx.shape[-1]
     gidx = idx.clamp_min(0).long()[..., None].expand(-1, -1, -1, D)
@@ -445,7 +625,42 @@ def hybrid_leg(args, flush):
                      "frac": round(alg / t_call / 1e9 / PEAK_HBM_GBS, 4),
                      "call_ms": round(t_call * 1e3, 4), "traffic": None},
         "cache": "flushed (512 MB read of another buffer) before every timed step",
+        "cpu_oracle": None if cpu is None else dict(cpu["decode"], GB_per_s=round(alg / cpu["decode_s"] / 1e9, 3)),
+        "selection_cpu_oracle": None if cpu is None else cpu["selection"],
     }
+
+
+def hybrid_cpu_oracle(d, picks, pairs, T, W):
+    """The oracle's selection (encode the 64 recent queries of the KV head's
+    four query heads and the keys, column mass, top 5%) on `picks` KV heads,
+    then its hybrid decode step on `pairs` with those sets; both scaled to
+    batch 8 x 8 KV heads (x 4 query heads)."""
+    import numpy as np
+    from oracle import mx, select
+
+    cores, info = host_cores()
+    k_rows = {key: _host(d["k"][key]) for key in picks}
+    v_rows = {key: _host(d["v"][key]) for key in picks}
+    sets, t_sel = {}, 0.0
+    for (b, kv) in picks:
+        qr = _host(d["q_recent"][b, 4 * kv:4 * kv + 4]).reshape(-1, k_rows[(b, kv)].shape[1])
+        t0 = time.perf_counter()
+        qc, qsb = mx.quantize(qr, axis=1)
+        kc, ksb = mx.quantize(k_rows[(b, kv)], axis=1)
+        cm = select.colmass_update(np.zeros(T), mx.dequantize(qc, qsb, 1), mx.dequantize(kc, ksb, 1), T)
+        sel = select.topk_vertical(cm, T, W, 5, 100)
+        t_sel += time.perf_counter() - t0
+        toks = np.concatenate([sel, np.arange(T - W, T)])
+        sets[(b, kv)] = (toks, k_rows[(b, kv)][toks], v_rows[(b, kv)][toks])
+    q_rows = {key: _host(d["q"][key]) for key in pairs}
+    dec = decode_cpu_oracle(k_rows, v_rows, q_rows, 8, 32, 8, T, 1, hybrid_sets=sets, q_bf=q_rows)
+    dec.pop("GB_per_s")
+    sel_full = 64 * t_sel / len(picks)
+    return {"decode": dec, "decode_s": dec["scaled_s"],
+            "selection": {"value": round(sel_full * 1e3, 1), "unit": "ms per selection call", "cores": cores,
+                          "kind": "oracle", "host": info,
+                          "sample": f"{len(picks)} KV heads: encode 256 recent queries and 32768 keys, column "
+                                    f"mass, top 5%; {t_sel:.2f} s measured, scaled to 64 KV heads"}}
 
 
 # ------------------------------------------------------------------ long non-causal
@@ -474,8 +689,20 @@ def diffusion_leg(args):
         attn()
 
     steps, warm = max(args.steps // 4, 3), max(args.warmup // 2, 1)
-    wall, kern = timed(step, steps, warm, attn)
+    wall, _ = timed(step, steps, warm)
+    kern, kern_med = launch_events(attn, steps)
     flops = 4 * D * B * H * S * S
+    cpu = None
+    if args.cpu:
+        import numpy as np
+        heads = [0, 13]
+        rng = np.random.default_rng(5005)
+        rows = [np.sort(rng.choice(S, size=256, replace=False)) for _ in heads]
+        idx = [torch.as_tensor(r, device="cuda") for r in rows]
+        qs = np.stack([_host(d["q"][0, h].index_select(0, ix)) for h, ix in zip(heads, idx)])[None]
+        ks = _host(d["k"][:, heads])
+        vs = _host(d["v"][:, heads])
+        cpu = diffusion_cpu_oracle(qs, ks, vs, heads, rows)
     del d, out
     torch.cuda.empty_cache()
     return {
@@ -488,12 +715,57 @@ def diffusion_leg(args):
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,128,non-causal,uos>",
                      "achieved": round(flops / kern / 1e12, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / kern / 1e12 / PEAK_FP4_TFLOPS, 4),
-                     "kernel_ms": round(kern * 1e3, 4), "traffic": None},
+                     "kernel_ms": round(kern * 1e3, 4), "kernel_median_ms": round(kern_med * 1e3, 4),
+                     "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,false,true> uos")},
+        "cpu_oracle": cpu,
     }
+
+
+def tiny_leg(args):
+    """The tiny workload (batch 1, one head, 128 x 64, fp16, non-causal, OCP):
+    quantise Q, K, V + attention; launch-bound, no roofline claim."""
+    import torch
+    import bit_microscaled_flashattention_amd as mxa
+    import synth
+
+    d = synth.tiny(device="cuda")
+    out = torch.empty((1, 1, 128, 64), dtype=torch.float32, device="cuda")
+
+    def step():
+        qh, kh = mxa.quantize(d["q"], "hd"), mxa.quantize(d["k"], "hd")
+        vh = mxa.quantize(d["v"], "key")
+        mxa.prefill(qh, kh, vh, causal=False, kv_tile=KV_TILE, out=out)
+
+    wall, _ = timed(step, args.steps, args.warmup)
+    res = {"workload": "batch 1, 1 head, seq 128, head_dim 64, fp16 N(0,1), non-causal, OCP, one 128-key tile; "
+                       "step = quantise Q, K, V (3 launches) + attention",
+           "ms_per_step": round(wall * 1e3, 4), "flops": 4 * 64 * 128 * 128,
+           "note": "launch-bound: four launches of a few microseconds each"}
+    if args.cpu:
+        res["cpu_oracle"] = tiny_cpu_oracle(d)
+    return res
+
+
+def hbm_reference():
+    """What torch's own kernels reach on this device, as context for the HBM
+    fractions: a sum over 4 GiB (read) and a 2 GiB device copy (read+write)."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.int32, device="cuda")
+    y = torch.empty(1 << 29, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("sum_read_4GiB", lambda: x.sum(), 4 << 30),
+                             ("copy_2GiB", lambda: y.copy_(x[: 1 << 29]), 4 << 30)):
+        mean, med = launch_events(fn, 5)
+        res[name] = {"GB_per_s": round(nbytes / med / 1e9, 1), "ms": round(med * 1e3, 3)}
+    del x, y
+    torch.cuda.empty_cache()
+    res["note"] = "torch kernels, median of 5 event-timed launches; bytes counted once each way"
+    return res
 
 
 def main():
     args = parse()
+    args.cpu = not args.no_cpu_baseline
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus must be 1 "
               "(multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
@@ -532,7 +804,12 @@ def main():
                      "achieved": round(pre["kernel_tflops"], 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre["kernel_tflops"] / PEAK_FP4_TFLOPS, 4),
                      "kernel_ms": round(pre["kernel_s"] * 1e3, 4),
+                     "kernel_median_ms": round(pre["kernel_median_s"] * 1e3, 4),
+                     "kernel_back_to_back_ms": round(pre["kernel_b2b_s"] * 1e3, 4),
+                     "timing": "kernel_ms: mean of per-launch event pairs on the launch stream, queue kept full; "
+                               "back_to_back: two events around all launches / launches",
                      "traffic": profiled_traffic("prefill", "prefill_kernel<128,128,true,true>")},
+        "bf16_out": pre["bf16_out"],
         "hadamard_qk": pre["hadamard_qk"],
         "hybrid_prefill": pre["hybrid_prefill"],
     }
@@ -549,9 +826,12 @@ def main():
             line["hybrid_decode"] = hybrid_leg(args, flush)
             torch.cuda.empty_cache()
         del flush
-    if not args.no_cpu_baseline:
+    if "tiny" in legs:
+        line["tiny"] = tiny_leg(args)
+    line["hbm_reference"] = hbm_reference()
+    if args.cpu:
         d2 = __import__("synth").gqa_prefill(device="cuda")
-        line["cpu_baseline"] = prefill_cpu_baseline(d2, cal)
+        line["cpu_baseline"], line["tile_mass_loss"] = prefill_cpu_baseline(d2, cal)
         del d2
     print(json.dumps(line), flush=True)
 
