@@ -35,7 +35,8 @@ METRIC = "MXFP4 attn prefill TFLOP/s; 32K decode ms/token + HBM GB/s (% roofline
 # Launch configurations the legs time (tests/test_gpu_bench_configs.py runs
 # the same calls against the oracle).
 KV_TILE = 128           # prefill key tile
-DECODE_SPLIT = 4096     # tokens per split, 32K batch-32 decode
+DECODE_SPLIT = 16384    # tokens per split, 32K batch-32 decode: 2 x 256 (sequence, KV head) = 512
+                        # workgroups, one round at two per CU
 HYBRID_SPLIT = 2752     # tokens per split, 32K batch-8 hybrid decode: 12 splits x 64 (sequence, KV head)
                         # = 768 workgroups, one round at three per CU
 HYBRID_WINDOW = 128     # bf16 recent window (decode and hybrid prefill)
@@ -46,11 +47,17 @@ HYBRID_WINDOW = 128     # bf16 recent window (decode and hybrid prefill)
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # fetch 6884.1 KiB x 2.000 + write 65540.0 KiB x 1.000 per dispatch (medians of 10)
-    "prefill_kernel<128,128,true,true>": {"bytes": 81211616, "sources": "c93be10ee1f0f879"},
-    # the one-call step (bf16 query encoded in the scan): fetch 558213 KiB x 2.000
-    # + write 4352 KiB x 1.000 per dispatch (medians of 3)
-    "decode_scan_kernel<128> split 4096": {"bytes": 1147676672, "sources": "70340a3ff903639e"},
+    # 4K causal GQA step: fetch 6883.2 KiB x 2.000 + write 65541.2 KiB x 1.000 per dispatch (median of 21)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81211104, "sources": "c93be10ee1f0f879"},
+    # 32K non-causal UOS (24 heads): fetch 1284943.8 KiB x 2 + write 393218.2 KiB (median of 8): K/V of a
+    # head re-read from the memory side by each of its 256 query blocks (three heads per XCD exceed its L2)
+    "prefill_kernel<128,128,false,true> uos": {"bytes": 3034220256, "sources": "c93be10ee1f0f879"},
+    # 32K batch-32 call (bf16 query encoded in the scan): scan fetch 557308 KiB x 2 + write 1088 KiB
+    # (median of 8), plus the merge (1750016 bytes)
+    "decode_scan_kernel<128> split 16384": {"bytes": 1144272000, "sources": "df608f45c739eb73"},
+    # 32K batch-8 hybrid call: scan 347713600 bytes (median of 8) + merge 2307072; the 4-bit rows of the
+    # bf16-held tokens are not fetched, but their 128-byte lines mostly hold a neighbour that is
+    "decode_scan_kernel<128> hybrid split 2752": {"bytes": 350020672, "sources": "df608f45c739eb73"},
 }
 TRAFFIC_SOURCES = {
     "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
@@ -514,8 +521,12 @@ def decode_leg(args, flush):
     del vc
     torch.cuda.empty_cache()
 
+    # A split spans at most 64 pages.
+    split_p = min(SPLIT, 64 * PAGE)
+    ws_p = torch.empty(mxa.decode_workspace_bytes(B, HQ, HKV, D, T, split_p), dtype=torch.uint8, device="cuda")
+
     def call_paged():
-        mxa.decode_paged(qbf, kp, vp, table, d["ctx_len"], split_len=SPLIT, workspace=ws, out=out)
+        mxa.decode_paged(qbf, kp, vp, table, d["ctx_len"], split_len=split_p, workspace=ws_p, out=out)
 
     t_call_p = timed_flushed(call_paged, args.steps, args.warmup, flush)
     cache_bytes = B * HKV * T * (D // 2 + D // 32) * 2
@@ -552,7 +563,7 @@ def decode_leg(args, flush):
             "call_ms": round(t_call_p * 1e3, 4),
             "achieved_GB_per_s": round(alg / t_call_p / 1e9, 1),
             "frac": round(alg / t_call_p / 1e9 / PEAK_HBM_GBS, 4),
-            "note": f"same cache as a shuffled pool of {PAGE}-token pages (block table [32, {maxp}])",
+            "note": f"same cache as a shuffled pool of {PAGE}-token pages (block table [32, {maxp}]), split {split_p}",
         },
     }
 
@@ -577,14 +588,18 @@ def hybrid_leg(args, flush):
     cpu = None
     if args.cpu:
         cpu = hybrid_cpu_oracle(d, [(1, 2), (6, 5)], [(1, 8), (1, 11), (6, 20), (6, 22)], T, W)
-    # Gather the bf16 rows of the selected tokens and of the window (caller side).
+    # Gather the bf16 rows of the selected tokens (the method keeps them in
+    # full precision), timed with the selection it follows.
     max_sel = idx.shape[-1]
-    gidx = idx.clamp_min(0).long()[..., None].expand(-1, -1, -1, D)
-    hy = {"idx": idx, "n_sel": n, "window": W,
-          "k_sel": torch.gather(d["k"], 2, gidx).contiguous(), "v_sel": torch.gather(d["v"], 2, gidx).contiguous(),
+    k_sel = torch.empty((B, HKV, max_sel, D), dtype=torch.bfloat16, device="cuda")
+    v_sel = torch.empty_like(k_sel)
+
+    def gather():
+        mxa.gather_rows(d["k"], d["v"], idx, n, k_sel, v_sel)
+
+    gather()
+    hy = {"idx": idx, "n_sel": n, "window": W, "k_sel": k_sel, "v_sel": v_sel,
           "k_win": d["k"][:, :, T - W:].contiguous(), "v_win": d["v"][:, :, T - W:].contiguous()}
-    del d["k"], d["v"]
-    torch.cuda.empty_cache()
     qh = mxa.empty_mx((B, HQ, 1, D), "hd")
     ws = torch.empty(mxa.decode_workspace_bytes(B, HQ, HKV, D, T, SPLIT, max_sel + W), dtype=torch.uint8,
                      device="cuda")
@@ -604,6 +619,9 @@ def hybrid_leg(args, flush):
     t_step = t_call
     t_step2 = timed_flushed(step_two_launches, args.steps, args.warmup, flush)
     t_sel = timed_flushed(select, max(args.steps // 4, 3), 1, flush)
+    t_gather = timed_flushed(gather, max(args.steps // 4, 3), 1, flush)
+    del d["k"], d["v"]
+    torch.cuda.empty_cache()
     nsel = int(n[0, 0].item())
     n4 = T - W - nsel
     per_pair = n4 * (D // 2 + D // 32) * 2 + (nsel + W) * D * 2 * 2 + nsel * 4
@@ -619,11 +637,15 @@ def hybrid_leg(args, flush):
         "bf16_overhead_of_nonwindow_kv": round(nsel * (2 * D * 2 - (D // 2 + D // 32) * 2) /
                                                ((T - W) * (D // 2 + D // 32) * 2), 4),
         "selection_ms": round(t_sel * 1e3, 4),
-        "selection_share_of_64_steps": round(t_sel / (t_sel + 64 * t_step), 4),
+        "gather_ms": round(t_gather * 1e3, 4),
+        "selection_share_of_64_steps": round((t_sel + t_gather) / (t_sel + t_gather + 64 * t_step), 4),
+        "selection_share_note": "(selection call + bf16 gather of the selected rows) / (that + 64 hybrid decode "
+                                "calls): one refresh every 64 tokens",
         "roofline": {"bound": "hbm", "kernel": "mxattn_decode hybrid (one scan launch: fp4 splits + bf16 parts; merge)",
                      "achieved": round(alg / t_call / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(alg / t_call / 1e9 / PEAK_HBM_GBS, 4),
-                     "call_ms": round(t_call * 1e3, 4), "traffic": None},
+                     "call_ms": round(t_call * 1e3, 4),
+                     "traffic": profiled_traffic("decode", f"decode_scan_kernel<128> hybrid split {SPLIT}")},
         "cache": "flushed (512 MB read of another buffer) before every timed step",
         "cpu_oracle": None if cpu is None else dict(cpu["decode"], GB_per_s=round(alg / cpu["decode_s"] / 1e9, 3)),
         "selection_cpu_oracle": None if cpu is None else cpu["selection"],
@@ -782,7 +804,29 @@ def main():
                           "sources": {k: sources_digest(k) for k in TRAFFIC_SOURCES}}))
         return
     legs = set(args.legs.split(","))
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if "prefill" not in legs:
+        # Profiling runs of single legs: no headline figure.
+        line = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "legs": sorted(legs)}
+        flush = _flush_buffer()
+        if "diffusion" in legs:
+            line["diffusion_prefill"] = diffusion_leg(args)
+            progress("diffusion leg done")
+        if "decode" in legs:
+            line["decode"] = decode_leg(args, flush)
+            torch.cuda.empty_cache()
+            progress("decode leg done")
+        if "hybrid" in legs:
+            line["hybrid_decode"] = hybrid_leg(args, flush)
+            progress("hybrid leg done")
+        print(json.dumps(line), flush=True)
+        return
     pre, d, cal = prefill_leg(args)
+    progress("prefill leg done")
     line = {
         "metric": METRIC,
         "value": round(pre["step_tflops"], 2),
@@ -817,19 +861,23 @@ def main():
     torch.cuda.empty_cache()
     if "diffusion" in legs:
         line["diffusion_prefill"] = diffusion_leg(args)
+        progress("diffusion leg done")
     if legs & {"decode", "hybrid"}:
         flush = _flush_buffer()
         if "decode" in legs:
             line["decode"] = decode_leg(args, flush)
             torch.cuda.empty_cache()
+            progress("decode leg done")
         if "hybrid" in legs:
             line["hybrid_decode"] = hybrid_leg(args, flush)
             torch.cuda.empty_cache()
+            progress("hybrid leg done")
         del flush
     if "tiny" in legs:
         line["tiny"] = tiny_leg(args)
     line["hbm_reference"] = hbm_reference()
     if args.cpu:
+        progress("timing the CPU oracle")
         d2 = __import__("synth").gqa_prefill(device="cuda")
         line["cpu_baseline"], line["tile_mass_loss"] = prefill_cpu_baseline(d2, cal)
         del d2

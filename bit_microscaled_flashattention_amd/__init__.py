@@ -103,6 +103,7 @@ def _load():
         "mxattn_decode_paged": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), P(_Paging), vp, P(_Hybrid), f32, i32, vp, sz,
                                 vp, vp, vp],
         "mxattn_decode_noalloc": [P(_Mx), P(_Mx), vp, P(_Mx), P(_Mx), vp, P(_Hybrid), f32, i32, vp, vp, vp],
+        "mxattn_gather_rows": [vp, vp, P(i64), P(i64), P(i64), vp, vp, i32, vp, vp, vp],
         "mxattn_quantize_dual": [vp, i32, P(i64), vp, i32, f32, i32, P(_Mx), P(_Mx), vp],
         "mxattn_select_vertical": [P(_Mx), P(_Mx), vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp],
     }
@@ -129,7 +130,7 @@ EXPORTS = (
     "mxattn_quantize", "mxattn_quantize_dual", "mxattn_quantize_batch", "mxattn_smooth_calibrate", "mxattn_prefill",
     "mxattn_prefill_hybrid",
     "mxattn_decode_workspace_bytes", "mxattn_decode", "mxattn_decode_paged", "mxattn_decode_noalloc",
-    "mxattn_select_workspace_bytes", "mxattn_select_vertical",
+    "mxattn_select_workspace_bytes", "mxattn_select_vertical", "mxattn_gather_rows",
     "mxattn_status_string", "mxattn_last_error", "mxattn_version",
 )
 
@@ -479,3 +480,34 @@ def select_vertical(q_recent, k_cache, ctx_len, col_mass, window, rho_num=5, rho
                                        int(rho_den), _ptr(col_mass), _ptr(idx), _ptr(n), int(max_sel),
                                        _ptr(workspace), workspace.numel(), _stream(k_cache.codes)))
     return idx, n
+
+
+def gather_rows(k, v, idx, n_sel, k_out=None, v_out=None):
+    """bf16 rows of the selected tokens: k_out[b,h,i] = k[b,h,idx[b,h,i]] for
+    i < n_sel[b,h] (k, v: bf16 [B,H,T,D] with contiguous channels; idx int32
+    [B,H,max_sel], n_sel int32 [B,H]).  Returns (k_out, v_out), bf16
+    [B,H,max_sel,D]; rows at or past n_sel are not written."""
+    b, h, t, d = k.shape
+
+    def need(cond, what):
+        if not cond:
+            raise ValueError(f"gather_rows: {what}")
+
+    need(k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and tuple(v.shape) == (b, h, t, d), "k, v bf16 [B,H,T,D]")
+    need(k.stride(3) == 1 and v.stride(3) == 1, "channels must be contiguous")
+    need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.dim() == 3 and tuple(idx.shape[:2]) == (b, h),
+         "idx contiguous int32 [B,H,max_sel]")
+    need(n_sel.dtype == torch.int32 and n_sel.is_contiguous() and tuple(n_sel.shape) == (b, h), "n_sel int32 [B,H]")
+    m = idx.shape[-1]
+    if k_out is None:
+        k_out = torch.empty((b, h, m, d), dtype=torch.bfloat16, device=k.device)
+    if v_out is None:
+        v_out = torch.empty((b, h, m, d), dtype=torch.bfloat16, device=k.device)
+    for o in (k_out, v_out):
+        need(o.dtype == torch.bfloat16 and o.is_contiguous() and tuple(o.shape) == (b, h, m, d), "outputs bf16 [B,H,max_sel,D]")
+    shape = (ctypes.c_int64 * 4)(b, h, t, d)
+    ks = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    vs = (ctypes.c_int64 * 3)(v.stride(0), v.stride(1), v.stride(2))
+    _check(_lib.mxattn_gather_rows(_ptr(k), _ptr(v), shape, ks, vs, _ptr(idx), _ptr(n_sel), int(m), _ptr(k_out),
+                                   _ptr(v_out), _stream(k)))
+    return k_out, v_out

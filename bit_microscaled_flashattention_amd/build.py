@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "prefill.hip", "decode.hip", "select.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "prefill.hip", "decode.hip", "select.hip", "gather.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -628,4 +628,43 @@ mxattn_status_t mxattn_select_vertical(const mxattn_mx_t* q, const mxattn_mx_t* 
   return after_launch(launch_select(a, static_cast<int>(kc->dim), s), s, "select_vertical");
 }
 
+mxattn_status_t mxattn_gather_rows(const void* k, const void* v, const int64_t shape[4], const int64_t k_stride[3],
+                                   const int64_t v_stride[3], const int32_t* idx, const int32_t* n_sel,
+                                   int32_t max_sel, void* k_out, void* v_out, mxattn_stream_t stream) {
+  mxattn_status_t st;
+  if (injected("gather_rows", &st)) return st;
+  if (!shape || !k_stride || !v_stride) return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: null shape/strides");
+  if (max_sel < 0) return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: negative max_sel");
+  const int64_t B = shape[0], H = shape[1], T = shape[2], D = shape[3];
+  if (B < 1 || H < 1 || T < 1) return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: empty shape");
+  if (D != 64 && D != 128) return fail(MXATTN_ERR_UNSUPPORTED, "gather_rows: head_dim %lld not in {64,128}", (long long)D);
+  if (B * H > 65535 || T > 0x7FFFFFFF) return fail(MXATTN_ERR_UNSUPPORTED, "gather_rows: batch x heads above 65535");
+  if (max_sel == 0) return ok();
+  if (!k || !v || !idx || !n_sel || !k_out || !v_out) return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: null pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: rows must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (k_stride[i] < 0 || v_stride[i] < 0 || (k_stride[i] * 2) % 16 != 0 || (v_stride[i] * 2) % 16 != 0)
+      return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: strides must be non-negative multiples of 8 elements");
+  if (k_stride[2] < D || v_stride[2] < D) return fail(MXATTN_ERR_INVALID_ARG, "gather_rows: row stride below D");
+  GatherArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  for (int i = 0; i < 3; ++i) {
+    a.ks[i] = k_stride[i];
+    a.vs[i] = v_stride[i];
+  }
+  a.idx = idx;
+  a.n_sel = n_sel;
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  a.B = static_cast<int>(B);
+  a.H = static_cast<int>(H);
+  a.T = static_cast<int>(T);
+  a.D = static_cast<int>(D);
+  a.max_sel = max_sel;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return after_launch(launch_gather_rows(a, s), s, "gather_rows");
+}
+
 }  // extern "C"

@@ -346,10 +346,14 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
       rvs = make_rsrc(a.v.scales + pp * a.v.ss[0] + hk * a.v.ss[1], rec * uint32_t(P * vss));
       tb = t_begin + pi * P;
     }
+    // Hybrid: tokens held in bf16 are not fetched from the 4-bit cache (their
+    // codes read as zeros; their logits are masked in `process`).
+    uint32_t selw = 0u;
+    if (a.hybrid && t0 < t_end) selw = selbits[(t0 - t_begin) >> 5];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = t0 + h * 16 + j;
-      const bool ok = t < t_end && g < nblk_d;
+      const bool ok = t < t_end && g < nblk_d && !((selw >> (h * 16 + j)) & 1u);
       const uint32_t oc = ok ? uint32_t((t - tb) * kcs + g * 16) : kOutOfRange;
       const uint32_t os = ok ? uint32_t((t - tb) * kss + g) : kOutOfRange;
       r.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rkc, oc, 0, kAuxStream);
@@ -360,7 +364,7 @@ __device__ __forceinline__ void fp4_split(const DecodeArgs& a, uint8_t* vstage, 
       const int bi = lane + 64 * h;
       const int tt = bi / nblk_d, db = bi % nblk_d;
       const int t = t0 + tt;
-      const bool ok = tt < kChunk && t < t_end;
+      const bool ok = tt < kChunk && t < t_end && !((selw >> (tt & 31)) & 1u);
       const uint32_t oc = ok ? uint32_t((t - tb) * vcs + db * 16) : kOutOfRange;
       const uint32_t os = ok ? uint32_t((t - tb) * vss + db) : kOutOfRange;
       r.v[h] = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 0, kAuxStream);

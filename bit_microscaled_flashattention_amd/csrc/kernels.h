@@ -147,6 +147,17 @@ struct SelectArgs {
   int32_t* n_out;
 };
 
+struct GatherArgs {
+  const uint16_t* k;    // bf16 [B][H][T][D], element strides ks / vs (D contiguous)
+  const uint16_t* v;
+  int64_t ks[3], vs[3];
+  const int32_t* idx;   // [B][H][max_sel]
+  const int32_t* n_sel; // [B][H]
+  uint16_t* k_out;      // bf16 [B][H][max_sel][D]
+  uint16_t* v_out;
+  int B, H, T, D, max_sel;
+};
+
 hipError_t launch_quantize_batch(const QuantArgs* jobs, int n, hipStream_t stream);
 hipError_t launch_smooth_calibrate(const CalibArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int kv_tile, int causal, hipStream_t stream);
@@ -158,5 +169,6 @@ constexpr size_t kDecodeScratchBytes = size_t{16} << 20;
 // device, then cached).
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream);
+hipError_t launch_gather_rows(const GatherArgs& a, hipStream_t stream);
 
 }  // namespace mxattn

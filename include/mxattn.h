@@ -387,6 +387,26 @@ const char* mxattn_status_string(mxattn_status_t status);
 const char* mxattn_last_error(void);
 const char* mxattn_version(void);
 
+/* ---------------------------------------------------------------------------
+ * mxattn_gather_rows -- the bf16 K and V rows of the selected tokens, copied
+ * into the contiguous arrays the hybrid decode reads (HyQuant, method
+ * paragraphs: the vertical-line tokens stay in full precision beside the
+ * 4-bit cache; the page does not say where those rows come from, so the
+ * caller keeps them and this call gathers them after each selection).
+ *   k, v        bf16 [B][H][T][D] (shape), element strides k_stride /
+ *               v_stride for the batch, head and token axes; channels
+ *               contiguous; rows 16-byte aligned.
+ *   idx, n_sel  device int32 [B][H][max_sel] and [B][H], as written by
+ *               mxattn_select_vertical; rows 0 .. n_sel-1 of each (b, h) are
+ *               copied (n_sel clamped to [0, max_sel] on the device).
+ *   k_out, v_out  bf16 [B][H][max_sel][D] contiguous (caller-owned): row i
+ *               holds token idx[b][h][i]; an index outside [0, T) gives a
+ *               zero row; rows at or past n_sel are left untouched.
+ * Supported: D in {64, 128}; B x H <= 65535.  max_sel = 0 does nothing. */
+mxattn_status_t mxattn_gather_rows(const void* k, const void* v, const int64_t shape[4], const int64_t k_stride[3],
+                                   const int64_t v_stride[3], const int32_t* idx, const int32_t* n_sel,
+                                   int32_t max_sel, void* k_out, void* v_out, mxattn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

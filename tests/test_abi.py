@@ -500,3 +500,33 @@ def test_decode_output_checked_in_binding(bad):
     lse = torch.zeros((b, hq + (bad == "lse_shape")))
     with pytest.raises(ValueError, match="out/lse"):
         mxa.decode_noalloc(q, cache, cache, torch.full((b,), t, dtype=torch.int32), out, split_len=128, lse=lse)
+
+
+def _gather(k=4096, v=8192, shape=(2, 4, 100, 128), ks=None, vs=None, idx=64, n=128, max_sel=16, ko=12288, vo=16384):
+    lib = mxa.library()
+    b, h, t, d = shape
+    st = (ctypes.c_int64 * 4)(*shape)
+    ks = (ctypes.c_int64 * 3)(*(ks or (h * t * d, t * d, d)))
+    vs = (ctypes.c_int64 * 3)(*(vs or (h * t * d, t * d, d)))
+    return lib.mxattn_gather_rows(ctypes.c_void_p(k), ctypes.c_void_p(v), st, ks, vs, ctypes.c_void_p(idx),
+                                  ctypes.c_void_p(n), max_sel, ctypes.c_void_p(ko), ctypes.c_void_p(vo), None)
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(shape=(2, 4, 100, 96)), mxa.ERR_UNSUPPORTED),
+    (dict(shape=(0, 4, 100, 128)), mxa.ERR_INVALID_ARG),
+    (dict(shape=(300, 300, 100, 128)), mxa.ERR_UNSUPPORTED),
+    (dict(max_sel=-1), mxa.ERR_INVALID_ARG),
+    (dict(k=4100), mxa.ERR_INVALID_ARG),
+    (dict(vo=0), mxa.ERR_INVALID_ARG),
+    (dict(ks=(51200, 12800, 100)), mxa.ERR_INVALID_ARG),
+    (dict(vs=(51200, 12800, 64)), mxa.ERR_INVALID_ARG),
+])
+def test_gather_rows_rejects(kw, status):
+    """Argument checks of mxattn_gather_rows, all on the host."""
+    assert _gather(**kw) == status, mxa.library().mxattn_last_error()
+    assert len(mxa.library().mxattn_last_error()) > 0
+
+
+def test_gather_rows_zero_rows_is_a_no_op():
+    assert _gather(max_sel=0, idx=0, n=0, ko=0, vo=0) == mxa.OK

@@ -192,9 +192,8 @@ def test_hybrid_decode_32k_batch8_bench_call():
         idx[b, kv] = torch.from_numpy(sel.astype(np.int32)).to(DEV)
         oracle_sets[(b, kv)] = sel
     # Gather the bf16 rows of the selected tokens and the window, as the benchmark does.
-    gidx = idx.clamp_min(0).long()[..., None].expand(-1, -1, -1, D)
-    hy = {"idx": idx, "n_sel": n, "window": W,
-          "k_sel": torch.gather(d["k"], 2, gidx).contiguous(), "v_sel": torch.gather(d["v"], 2, gidx).contiguous(),
+    k_sel, v_sel = mxa.gather_rows(d["k"], d["v"], idx, n)
+    hy = {"idx": idx, "n_sel": n, "window": W, "k_sel": k_sel, "v_sel": v_sel,
           "k_win": d["k"][:, :, T - W:].contiguous(), "v_win": d["v"][:, :, T - W:].contiguous()}
     qbf = d["q"].contiguous()
     print(f"hybrid decode 32K batch 8 bench call, split {bench.HYBRID_SPLIT}", flush=True)

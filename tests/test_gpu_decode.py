@@ -497,3 +497,42 @@ def test_decode_degenerate_zero_query_gives_mean():
         for h in range(hq):
             np.testing.assert_allclose(out[bb, h].cpu().numpy(), vd[bb, h // 2, :c].mean(axis=0), atol=1e-5, rtol=0)
             assert abs(float(lse[bb, h]) - np.log(c)) < 1e-5
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_gather_rows_matches_host_indexing(d):
+    """mxattn_gather_rows against numpy fancy indexing on host copies, bit for
+    bit: strided K (a view of a wider cache), ragged n_sel, indices outside
+    [0, T) (zero rows), rows past n_sel left as they were."""
+    g = torch.Generator(device=DEV).manual_seed(95)
+    b, h, t, m = 2, 3, 1000, 40
+    kbig = torch.randn((b, h, t + 24, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = kbig[:, :, 10:10 + t]                      # token-strided view
+    v = torch.randn((b, h, t, d), generator=g, device=DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(96)
+    idx = rng.integers(0, t, size=(b, h, m)).astype(np.int32)
+    idx[0, 1, 3] = -1
+    idx[1, 2, 5] = t + 7
+    nsel = np.array([[m, 17, 0], [1, m, 33]], dtype=np.int32)
+    ko = torch.full((b, h, m, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    vo = torch.full_like(ko, -3.0)
+    print(f"gather rows d={d}", flush=True)
+    mxa.gather_rows(k, v, torch.from_numpy(idx).to(DEV), torch.from_numpy(nsel).to(DEV), ko, vo)
+    torch.cuda.synchronize()
+    kh = k.cpu().view(torch.int16).numpy()
+    vh = v.cpu().view(torch.int16).numpy()
+    gk, gv = ko.cpu().view(torch.int16).numpy(), vo.cpu().view(torch.int16).numpy()
+    seven = torch.tensor(7.0, dtype=torch.bfloat16).view(torch.int16).item()
+    mthree = torch.tensor(-3.0, dtype=torch.bfloat16).view(torch.int16).item()
+    for bb in range(b):
+        for hh in range(h):
+            n = int(nsel[bb, hh])
+            for i in range(m):
+                tt = int(idx[bb, hh, i])
+                if i >= n:
+                    assert (gk[bb, hh, i] == seven).all() and (gv[bb, hh, i] == mthree).all()
+                elif 0 <= tt < t:
+                    np.testing.assert_array_equal(gk[bb, hh, i], kh[bb, hh, tt])
+                    np.testing.assert_array_equal(gv[bb, hh, i], vh[bb, hh, tt])
+                else:
+                    assert (gk[bb, hh, i] == 0).all() and (gv[bb, hh, i] == 0).all()
