@@ -425,8 +425,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int qb,
     if (jt + 1 < nt) issue_tile<D, BC>(src, t0 + BC, next, sr, tid, wave_s);
     auto tile = [&]() {
       const uint8_t* base = smem + (jt & 1) * C::STAGE;
-      // Selected-key bitmap words of the tile's key blocks, read before the
-      // operands so that waiting for them leaves those loads in flight.
+      // Selected-key bitmap words of the tile's key blocks, read with the
+      // operands and made scalar after them, so the wait for them leaves
+      // those loads in flight.
       uint32_t selw[C::KB];
       if constexpr (HYB) {
         if constexpr (C::KB >= 4) {
@@ -440,8 +441,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int qb,
 #pragma unroll
           for (int e = 0; e < C::KB; ++e) selw[e] = selmap[(t0 >> 5) + e];
         }
-#pragma unroll
-        for (int e = 0; e < C::KB; ++e) selw[e] = __builtin_amdgcn_readfirstlane(selw[e]);
       }
 
       // Key block kb of this tile is [tb, tb + 32), tb = t0 + 32 kb.  Against
@@ -456,12 +455,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int qb,
         return !FULL && (tb + 32 > a.Sk || (CAUSAL && tb + 31 > lo_q));
       };
       // Logits of block kb: S^T = K_hat Q_hat^T over the D/64 chunks.
-      auto logits = [&](int kb) -> v16f {
-        v4i aop[C::DC];
+      // Every K operand and scale word of the tile is read before the first
+      // logit MFMA (the scheduling barrier keeps the reads together), so the
+      // tile pays the LDS latency once instead of once per key block.
+      v4i kop[C::KB][C::DC];
+      int ksws[(C::KB + C::KPD - 1) / C::KPD];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        if (blk_empty(kb)) continue;
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
-          aop[dc] = *reinterpret_cast<const v4i*>(base + koff[dc] + kb * 32 * C::KRB);
-        const int ksw = *reinterpret_cast<const int*>(base + ksoff + (kb / C::KPD) * 256);
+          kop[kb][dc] = *reinterpret_cast<const v4i*>(base + koff[dc] + kb * 32 * C::KRB);
+      }
+#pragma unroll
+      for (int g = 0; g < (C::KB + C::KPD - 1) / C::KPD; ++g)
+        ksws[g] = *reinterpret_cast<const int*>(base + ksoff + g * 256);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HYB) {
+#pragma unroll
+        for (int e = 0; e < C::KB; ++e) selw[e] = __builtin_amdgcn_readfirstlane(selw[e]);
+      }
+      auto logits = [&](int kb) -> v16f {
+        const v4i* aop = kop[kb];
+        const int ksw = ksws[kb / C::KPD];
         v16f acc = v16f{};
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc)
