@@ -391,7 +391,24 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectArgs a)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = cc * kTopkThreads * 4 + tid * 4 + u;
-          if (i < n && (x[cc][u] & pmask) == tau_bits) atomicAdd(&hist[wave][(x[cc][u] >> shift) & 255u], 1u);
+          const bool on = i < n && (x[cc][u] & pmask) == tau_bits;
+          const uint32_t dg = (x[cc][u] >> shift) & 255u;
+          if (shift == 24) {
+            // The top digit (sign and high exponent bits) takes few distinct
+            // values, so most lanes of a wave would add to the same counter
+            // at once.  Lanes with equal digits are counted by ballot and one
+            // of them adds the count.
+            uint64_t act = __ballot(on);
+            while (act != 0ull) {
+              const int leader = __builtin_ctzll(act);
+              const uint32_t dl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dg), leader));
+              const uint64_t same = __ballot(on && dg == dl);
+              if (lane == leader) atomicAdd(&hist[wave][dl], static_cast<uint32_t>(__popcll(same)));
+              act &= ~same;
+            }
+          } else if (on) {
+            atomicAdd(&hist[wave][dg], 1u);
+          }
         }
       }
       __syncthreads();
