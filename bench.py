@@ -203,6 +203,9 @@ def prefill_leg(args):
     settle_clocks(step)
     wall, kern_b2b = timed(step, args.steps, args.warmup, attn)
     kern, kern_med = launch_events(attn, args.steps)
+    # The step's output on the heads the CPU oracle later recomputes, for the
+    # full-size comparison reported beside the oracle's time (untimed).
+    out_sample = out[:, list(range(0, HQ, 3))].cpu()
     # The same kernel writing bf16 outputs (half the output bytes).
     out_bf = torch.empty((B, HQ, S, D), dtype=torch.bfloat16, device="cuda")
 
@@ -244,7 +247,7 @@ def prefill_leg(args):
     res = {
         "flops": flops, "step_s": wall, "kernel_s": kern, "kernel_median_s": kern_med, "kernel_b2b_s": kern_b2b,
         "step_tflops": flops / wall / 1e12, "kernel_tflops": flops / kern / 1e12,
-        "quantize_s": quant,
+        "quantize_s": quant, "out_sample": out_sample,
         "bf16_out": {"kernel_ms": round(kern_bf * 1e3, 4), "kernel_median_ms": round(kern_bf_med * 1e3, 4),
                      "kernel_tflops": round(flops / kern_bf / 1e12, 2),
                      "frac": round(flops / kern_bf / 1e12 / PEAK_FP4_TFLOPS, 4),
@@ -287,13 +290,14 @@ def _host(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def prefill_cpu_baseline(d, cal):
+def prefill_cpu_baseline(d, cal, gpu_out=None):
     """The oracle on 11 of the 32 query heads (every third head), every row:
-    quantisation of those heads' Q, K, V plus the tiled prefill.  Rate scaled
-    to the full workload by the fraction of query-key pairs.  The same run
-    records the per-tile mass change of P quantisation (HiFA4's tile
-    diagnostic): eps = sum P_hat / sum P_tilde - 1 per (query row, 128-key
-    tile)."""
+    quantisation of those heads' Q, K, V plus the tiled prefill with its
+    rounding envelope.  Rate scaled to the full workload by the fraction of
+    query-key pairs.  The same run records the per-tile mass change of P
+    quantisation (HiFA4's tile diagnostic): eps = sum P_hat / sum P_tilde - 1
+    per (query row, 128-key tile), and, given the GPU step's output on those
+    heads, compares every row: |gpu - oracle| <= 2e-3 + envelope."""
     import numpy as np
     from oracle import attention, mx, smooth
 
@@ -305,6 +309,7 @@ def prefill_cpu_baseline(d, cal):
     v = _host(d["v"])
     S, D = q.shape[2], q.shape[3]
     eps = []
+    par = {"rows": 0, "max_abs_err": 0.0, "rows_with_envelope": 0, "rows_over_bar": 0}
     t0 = time.perf_counter()
     pairs = 0
     for i, h in enumerate(heads):
@@ -316,10 +321,17 @@ def prefill_cpu_baseline(d, cal):
         vc, vsb = mx.quantize(v[:, kv:kv + 1], axis=2)
         res = attention.prefill_head(mx.dequantize(qc, qsb, 3)[0, 0], mx.dequantize(kc, ksb, 3)[0, 0],
                                      mx.dequantize(vc, vsb, 2)[0, 0], causal=True, kv_tile=KV_TILE,
-                                     return_tile_eps=True)
+                                     envelope=True, return_tile_eps=True)
         e = res["tile_eps"]
         eps.append(e[np.isfinite(e)])
         pairs += S * (S + 1) // 2
+        if gpu_out is not None:
+            err = np.abs(gpu_out[0, i].numpy().astype(np.float64) - res["out"]).max(axis=1)
+            bnd = res["bound"]
+            par["max_abs_err"] = max(par["max_abs_err"], float(err.max()))
+            par["rows_with_envelope"] += int((bnd > 0).sum())
+            par["rows_over_bar"] += int((err > 2e-3 + bnd).sum())
+            par["rows"] += int(err.size)
     dt = time.perf_counter() - t0
     eps = np.concatenate(eps)
     out = {"value": 4 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -331,6 +343,10 @@ def prefill_cpu_baseline(d, cal):
             "tiles": int(eps.size),
             "note": "per (query row, 128-key tile): sum P_hat / sum P_tilde - 1 under OCP P scales, oracle, "
                     "the 11 sampled heads of the 4K step"}
+    if gpu_out is not None:
+        par["note"] = ("the timed step's fp32 output against the oracle on the same 11 heads, every row: "
+                       "max |gpu - oracle| per row against 2e-3 + the oracle's rounding envelope")
+        out["parity"] = par
     return out, tile
 
 
@@ -905,7 +921,7 @@ def main():
     if args.cpu:
         progress("timing the CPU oracle")
         d2 = __import__("synth").gqa_prefill(device="cuda")
-        line["cpu_baseline"], line["tile_mass_loss"] = prefill_cpu_baseline(d2, cal)
+        line["cpu_baseline"], line["tile_mass_loss"] = prefill_cpu_baseline(d2, cal, pre["out_sample"])
         del d2
     print(json.dumps(line), flush=True)
 
