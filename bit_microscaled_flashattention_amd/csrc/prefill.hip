@@ -574,9 +574,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int qb,
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts), __float_as_uint(ts), false, false);
             lsum += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
           }
-          uint32_t w0, w1;
-          asm("" : "=v"(w0));
-          asm("" : "=v"(w1));
+          // Each word's chain of converts starts from the register of its
+          // first input, which is dead after that convert (every byte is
+          // overwritten), so no placeholder value has to be copied in.
+          uint32_t w0 = __float_as_uint(p[0]), w1 = __float_as_uint(p[8]);
           w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[0], p[1], scl, 0);
           w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, p[8], p[9], scl, 0);
           w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, p[2], p[3], scl, 1);
