@@ -364,7 +364,7 @@ static mxattn_status_t prefill_common(const mxattn_mx_t* q, const mxattn_mx_t* k
     const int n_cu = device_cu_count();
     if (n_cu > 0 && static_cast<int64_t>(a.n_qblk) * a.B * a.Hq == 4LL * n_cu) {
       a.paired = 1;
-      a.pair_c = (27 * (a.n_qblk + 1) + 50) / 100;   // heavy pairs hold about 1.27x the mean tiles
+      a.pair_c = a.n_qblk / 4;   // every light pair then holds 3N/4 + 1 tiles
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

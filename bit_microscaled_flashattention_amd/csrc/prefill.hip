@@ -289,13 +289,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // two query blocks of one query head in turn.  On this GPU the workgroups
 // of a CU are issued oldest first: the one dispatched first (the lower
 // half of the grid when the grid fills every CU twice) runs about 1.8x
-// faster than its neighbour.  So the first half takes pairs of about 1.27x
-// the mean tiles and the second half the rest, and the two on a CU finish
-// together instead of one running alone at the end.  With N query blocks
-// per head (N % 4 == 0) and c = a.pair_c, the heavy pairs are
-// (N-1-i, c+i), i < N/4; the light pairs take the remaining blocks
-// smallest with largest.  Each XCD (bid % 8) works on whole KV heads, as in
-// map_block.  qb2 = -1: no second block.
+// faster than its neighbour.  So the first half takes the heavier pairs and
+// the second half the rest, and the two on a CU finish together instead of
+// one running alone at the end.  With N query blocks per head (N % 4 == 0)
+// and c = a.pair_c, the heavy pairs are (N-1-i, c+i), i < N/4; the light
+// pairs take the remaining blocks smallest with largest.  At c = N/4 every
+// heavy pair holds 5N/4 + 1 tiles and every light pair 3N/4 + 1.  Each XCD
+// (bid % 8) works on whole KV heads, as in map_block.  qb2 = -1: no second
+// block.
 __device__ __forceinline__ void map_pair(const PrefillArgs& a, int& qb1, int& qb2, int& b, int& hq) {
   const int G = a.Hq / a.Hkv;
   const int N = a.n_qblk, N4 = N / 4;
