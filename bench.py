@@ -47,11 +47,11 @@ HYBRID_WINDOW = 128     # bf16 recent window (decode and hybrid prefill)
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # 4K causal GQA step: fetch 6883.0 KiB x 2.000 + write 65540.25 KiB x 1.000 per dispatch (medians)
-    "prefill_kernel<128,128,true,true>": {"bytes": 81209600, "sources": "eba4adca17437212"},
-    # 32K non-causal UOS (24 heads): fetch 1267461.4 KiB x 2 + write 393218.8 KiB (median of 8): K/V of a
+    # 4K causal GQA step: fetch 6840.69 KiB x 2.000 + write 65579.34 KiB x 1.000 per dispatch (medians)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81162976, "sources": "875cbd3269e8a052"},
+    # 32K non-causal UOS (24 heads): fetch 1267412.4 KiB x 2 + write 393218.0 KiB (median of 8): K/V of a
     # head re-read from the memory side by each of its 256 query blocks (three heads per XCD exceed its L2)
-    "prefill_kernel<128,128,false,true> uos": {"bytes": 2998417104, "sources": "eba4adca17437212"},
+    "prefill_kernel<128,128,false,true> uos": {"bytes": 2998315952, "sources": "875cbd3269e8a052"},
     # 32K batch-32 call (bf16 query encoded in the scan): scan fetch 557308 KiB x 2 + write 1088 KiB
     # (median of 8), plus the merge (1750016 bytes)
     "decode_scan_kernel<128> split 16384": {"bytes": 1144272000, "sources": "df608f45c739eb73"},
