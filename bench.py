@@ -827,7 +827,7 @@ def main():
     args = parse()
     args.cpu = not args.no_cpu_baseline
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus must be 1 "
+        print("bench.py: the library runs on one GPU; --gpus must be 1 "
               "(multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
         sys.exit(2)
     import torch
