@@ -203,9 +203,6 @@ def prefill_leg(args):
     settle_clocks(step)
     wall, kern_b2b = timed(step, args.steps, args.warmup, attn)
     kern, kern_med = launch_events(attn, args.steps)
-    # The step's output on the heads the CPU oracle later recomputes, for the
-    # full-size comparison reported beside the oracle's time (untimed).
-    out_sample = out[:, list(range(0, HQ, 3))].cpu()
     # The same kernel writing bf16 outputs (half the output bytes).
     out_bf = torch.empty((B, HQ, S, D), dtype=torch.bfloat16, device="cuda")
 
@@ -242,6 +239,11 @@ def prefill_leg(args):
 
     wall_h, kern_h = timed(step_h, args.steps, args.warmup, attn_h)
     _, sel_t = timed(lambda: None, args.steps, 0, select)
+    # The plain step's output on the heads the CPU oracle later recomputes,
+    # for the full-size comparison reported beside the oracle's time.  Taken
+    # after all timing: the host copy idles the GPU, and its clocks drop.
+    step()
+    out_sample = out[:, list(range(0, HQ, 3))].cpu()
     pairs = B * HQ * S * (S + 1) // 2
     flops = 4 * D * pairs
     res = {
@@ -808,18 +810,27 @@ def tiny_leg(args):
 
 def hbm_reference():
     """What torch's own kernels reach on this device, as context for the HBM
-    fractions: a sum over 4 GiB (read) and a 2 GiB device copy (read+write)."""
+    fractions: a bf16 matrix-vector product over a 2 GiB matrix (a streaming
+    read: the vendor BLAS kernel, the fastest read measured here), a sum over
+    4 GiB (read) and a 2 GiB device copy (read+write)."""
     import torch
+    res = {}
+    a = torch.ones((1 << 20, 1024), dtype=torch.bfloat16, device="cuda")
+    xv = torch.ones(1024, dtype=torch.bfloat16, device="cuda")
+    settle_clocks(lambda: torch.mv(a, xv), 0.2)
+    mean, med = launch_events(lambda: torch.mv(a, xv), 20)
+    res["gemv_read_2GiB"] = {"GB_per_s": round((2 << 30) / med / 1e9, 1), "ms": round(med * 1e3, 3)}
+    del a, xv
     x = torch.ones(1 << 30, dtype=torch.int32, device="cuda")
     y = torch.empty(1 << 29, dtype=torch.int32, device="cuda")
-    res = {}
     for name, fn, nbytes in (("sum_read_4GiB", lambda: x.sum(), 4 << 30),
                              ("copy_2GiB", lambda: y.copy_(x[: 1 << 29]), 4 << 30)):
         mean, med = launch_events(fn, 5)
         res[name] = {"GB_per_s": round(nbytes / med / 1e9, 1), "ms": round(med * 1e3, 3)}
     del x, y
     torch.cuda.empty_cache()
-    res["note"] = "torch kernels, median of 5 event-timed launches; bytes counted once each way"
+    res["note"] = ("torch kernels, median of event-timed launches; bytes counted once each way; the matrix-vector "
+                   "product is the practical read ceiling against which the decode scans' fractions can be read")
     return res
 
 
