@@ -111,8 +111,8 @@ def test_hybrid_prefill_4k_gqa_bench_step():
 def test_diffusion_prefill_bench_step(group):
     """Batch 1, 24 heads, S 32768, D 128, UOS (Qmax 7.25) on Q, K, V and P,
     one quantiser launch + the non-causal kernel, as the benchmark runs it.
-    Heads 6*group .. 6*group+5: all K/V codes, and 32 seeded rows plus the
-    query-block and tile edges of each head against the oracle."""
+    Heads 6*group .. 6*group+5: all K/V codes, and 256 rows of each head
+    (245 seeded plus the query-block and tile edges) against the oracle."""
     d = synth.diffusion(device=DEV)
     print(f"diffusion bench step, heads {6 * group}..{6 * group + 5}", flush=True)
     qh, kh, vh = mxa.quantize_batch([dict(x=d["q"], rule="uos"), dict(x=d["k"], rule="uos"),
@@ -120,7 +120,7 @@ def test_diffusion_prefill_bench_step(group):
     out, lse = mxa.prefill(qh, kh, vh, causal=False, kv_tile=bench.KV_TILE, p_rule="uos", return_lse=True)
     torch.cuda.synchronize()
     heads = list(range(6 * group, 6 * group + 6))
-    rows = _rows(32768, 32, 60 + group, heads, [0, 1, 127, 128, 255, 256, 16383, 16384, 32639, 32640, 32767])
+    rows = _rows(32768, 245, 60 + group, heads, [0, 1, 127, 128, 255, 256, 16383, 16384, 32639, 32640, 32767])
     check_prefill(d["q"], d["k"], d["v"], qh, kh, vh, out, lse, causal=False, kv_tile=bench.KV_TILE,
                   p_rule="uos", qkv_rule="uos", rows=rows, heads=heads, q_rows_only=True,
                   what=f"diffusion heads {heads[0]}-{heads[-1]}")
