@@ -146,7 +146,7 @@ def _compare_group(out, lse, ref, b, kv, g, what):
 
 def test_decode_32k_batch32_bench_call():
     """Batch 32, 32/8 heads, ctx 32768, the benchmark's one call per token:
-    the bf16 query encoded inside the scan, split 4096, merge.  The four
+    the bf16 query encoded inside the scan, the benchmark's split, merge.  The four
     query heads of four seeded (sequence, KV head) pairs against the oracle
     (query encoded by the oracle from the same bf16 values)."""
     d = synth.long_decode(device=DEV)
