@@ -191,6 +191,70 @@ __device__ __forceinline__ void quantize_hd(const QuantArgs& a, int x, int64_t h
   }
 }
 
+
+// The same encoding for the common case: a workgroup inside one (batch,
+// head), no rotation, no residual.  The (batch, head) bases are then
+// uniform, so each lane's addresses are its row and channel only; this
+// takes the 4K step's Q launch from 12.5 to 10.8 us against the general
+// form above (same codes).
+template <int DT>
+__device__ __forceinline__ void quantize_hd_head(const QuantArgs& a, int x, int64_t h, int64_t b) {
+  const int nblk_row = static_cast<int>(a.D) / 32;   // 2 or 4
+  const int total = static_cast<int>(a.S) * nblk_row;
+  const int lane = threadIdx.x & 63, part = lane & 3;
+  const int wave = x * 4 + (threadIdx.x >> 6);
+  constexpr int kElem = DT == 0 ? 4 : 2;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x) + (b * a.xs[0] + h * a.xs[1]) * kElem;
+  uint8_t* cb = a.codes + b * a.cs[0] + h * a.cs[1];
+  uint8_t* sbp = a.scales + b * a.ss[0] + h * a.ss[1];
+  // Groups of 16 blocks start on a row boundary, so a lane's channels are
+  // the same in every group it handles.
+  const int db = (lane >> 2) & (nblk_row - 1);
+  const int d0 = db * 32 + part * 8;
+  int row[kHdRows];
+  bool on[kHdRows];
+  float y[kHdRows][8];
+#pragma unroll
+  for (int r = 0; r < kHdRows; ++r) {
+    const int blk = (wave * kHdRows + r) * 16 + (lane >> 2);
+    on[r] = blk < total;
+    row[r] = blk / nblk_row;
+    if (on[r]) {
+      load8<DT>(xb + static_cast<int64_t>(row[r]) * a.xs[2] * kElem, d0, y[r]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[r][k] = 0.0f;
+    }
+  }
+  if (a.chan_scale != nullptr) {
+    const v4f c0 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0);
+    const v4f c1 = *reinterpret_cast<const v4f*>(a.chan_scale + h * a.D + d0 + 4);
+#pragma unroll
+    for (int r = 0; r < kHdRows; ++r)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[r][k] = __fmul_rn(y[r][k], c0[k]);
+        y[r][4 + k] = __fmul_rn(y[r][4 + k], c1[k]);
+      }
+  }
+#pragma unroll
+  for (int r = 0; r < kHdRows; ++r) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = __float_as_uint(y[r][i]) & 0x7FFFFFFFu;
+      amax = m > amax ? m : amax;
+    }
+    // Lanes of a quad share the block, so a quad past the end is dead as a whole.
+    amax = quad_max(amax);
+    const int sb = e8m0_byte(amax, a.uos, a.qmax_quarter);
+    const uint32_t packed = encode8(y[r], sb);
+    if (!on[r]) continue;
+    *reinterpret_cast<uint32_t*>(cb + static_cast<int64_t>(row[r]) * a.cs[2] + d0 / 2) = packed;
+    if (part == 0) sbp[static_cast<int64_t>(row[r]) * a.ss[2] + db] = static_cast<uint8_t>(sb);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Sequence blocks (the key-blocked V layout of prefill).  Workgroup x of
 // (b, h) stages tokens [32x, 32x+32) x D channels in LDS as fp32 (16-byte
@@ -284,6 +348,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantBatch p) {
     if (a.dtype == 2) quantize_key<2>(a, x, h, b, tile);
     else if (a.dtype == 1) quantize_key<1>(a, x, h, b, tile);
     else quantize_key<0>(a, x, h, b, tile);
+  } else if (!a.hadamard && a.codes2 == nullptr) {
+    if (a.dtype == 2) quantize_hd_head<2>(a, x, h, b);
+    else if (a.dtype == 1) quantize_hd_head<1>(a, x, h, b);
+    else quantize_hd_head<0>(a, x, h, b);
   } else {
     if (a.dtype == 2) quantize_hd<2>(a, x, h, b, false);
     else if (a.dtype == 1) quantize_hd<1>(a, x, h, b, false);
