@@ -16,10 +16,11 @@
 //               to col_mass.  Each key belongs to exactly one lane: no atomics.
 //   topk     -- per (batch, KV head), one 1024-thread workgroup holding the
 //               masses in registers: the k-th largest fp32 bit pattern found
-//               by a radix select over 8-bit digits (bit patterns of
-//               non-negative values order like the values), then one ordered
-//               compaction that emits the indices ascending, ties at the
-//               threshold going to the lower indices.
+//               by a radix select over 12-, 10- and 10-bit digits (bit
+//               patterns of non-negative values order like the values), then
+//               one ordered compaction, a single prefix scan, that emits the
+//               indices ascending, ties at the threshold going to the lower
+//               indices.
 #include <type_traits>
 
 #include "mx_device.h"
@@ -116,13 +117,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sel_rsrc(const void* base, int
 // and row sum over the chunk.  The queries sit in LDS; wave w takes the
 // chunk's 32-key blocks w, w+4, ... for all query groups (K read once), and
 // the four waves' (max, sum) are merged in LDS at the end.
-constexpr int kStatGroups = kMaxRecent / 32;
-
-template <int D>
+//
+// NG is the largest number of 32-query groups the instance holds (8 or 16):
+// the per-query state and the LDS are sized by it, so the common case of 256
+// recent queries x group size keeps four workgroups per CU.
+template <int D, int NG>
 __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kMaxRecent * (D / 2)];
-  __shared__ uint8_t qs_lds[kMaxRecent * (D / 32)];
-  __shared__ float red[4][kMaxRecent][2];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[NG * 32 * (D / 2)];
+  __shared__ uint8_t qs_lds[NG * 32 * (D / 32)];
+  // The waves' (max, sum) per query reuse the query codes' LDS after the scan.
+  static_assert(4 * NG * 32 * 2 * sizeof(float) <= sizeof(q_lds), "reduction does not fit");
+  float (*red)[NG * 32][2] = reinterpret_cast<float (*)[NG * 32][2]>(q_lds);
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 31, hh = lane >> 5;
@@ -136,9 +141,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs
   const __amdgpu_buffer_rsrc_t rc = sel_rsrc(a.k.codes + b * a.k.cs[0] + hk * a.k.cs[1], int64_t(ctx) * a.k.cs[2]);
   const __amdgpu_buffer_rsrc_t rs = sel_rsrc(a.k.scales + b * a.k.ss[0] + hk * a.k.ss[1], int64_t(ctx) * a.k.ss[2]);
   const int kcs = static_cast<int>(a.k.cs[2]), kss = static_cast<int>(a.k.ss[2]);
-  float m[kStatGroups], l[kStatGroups];
+  float m[NG], l[NG];
 #pragma unroll
-  for (int g = 0; g < kStatGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     m[g] = -__builtin_huge_valf();
     l[g] = 0.0f;
   }
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs
     auto groups = [&](auto tail_tag) {
       constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
-      for (int g = 0; g < kStatGroups; ++g) {
+      for (int g = 0; g < NG; ++g) {
         if (g >= ng) continue;   // uniform; the loop stays unrolled, m[g]/l[g] in fixed registers
         // B operand: query g*32 + j from LDS.
         const int qi = g * 32 + j;
@@ -190,8 +195,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs
   }
   // This wave's (max, sum) per query (the two lane halves hold halves of the
   // sum), then the ordered merge of the four waves.
+  __syncthreads();   // every wave is done reading q_lds
 #pragma unroll
-  for (int g = 0; g < kStatGroups; ++g) {
+  for (int g = 0; g < NG; ++g) {
     if (g >= ng) continue;
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[g]), __float_as_uint(l[g]), false, false);
     const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
@@ -244,11 +250,11 @@ __global__ __launch_bounds__(kSelThreads) void select_finalize_kernel(SelectArgs
 // key belongs to one lane pair: no atomics.
 constexpr int kCmKeys = 512;
 
-template <int D>
+template <int D, int NG>
 __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kMaxRecent * (D / 2)];
-  __shared__ uint8_t qs_lds[kMaxRecent * (D / 32)];
-  __shared__ __attribute__((aligned(16))) float mc_lds[kMaxRecent + 32], il_lds[kMaxRecent + 32];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[NG * 32 * (D / 2)];
+  __shared__ uint8_t qs_lds[NG * 32 * (D / 32)];
+  __shared__ __attribute__((aligned(16))) float mc_lds[NG * 32], il_lds[NG * 32];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int G = a.Hq / a.Hkv;
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs 
     // Unrolled over the largest group count with a uniform skip, so the next
     // group's MFMAs can issue while this group's exponentials run.
 #pragma unroll
-    for (int g = 0; g < kStatGroups; ++g) {
+    for (int g = 0; g < NG; ++g) {
       if (g >= ng) continue;
       // A operand: queries g*32 + (lane % 32) from LDS.
       const int qa = g * 32 + j;
@@ -316,17 +322,37 @@ __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs 
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+// Radix digits from the top of the fp32 bit pattern: 12 bits (sign, exponent
+// and three mantissa bits, so the masses of one binade fall on 8 counters),
+// then 10 and 10.  The counters have eight copies, lane l adding to copy
+// l % 8; the copies are 4 words out of bank step, so lanes of one atomic
+// instruction that meet the same digit hit up to eight different banks.
+constexpr int kTkBits0 = 12, kTkBits1 = 10;
+constexpr int kTkCopies = 8;
+constexpr int kTkStride = (1 << kTkBits0) + 4;            // words per copy
+constexpr int kTopkStage = kTkCopies * (1 << kTkBits0);   // indices staged in the counters' LDS
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes (DPP row_shr; a source outside the row reads
+// as the 0 passed for `old`), then the totals of the lower rows, read from
+// lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_scan_incl(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
 
 // Inclusive prefix sum over the 1024 threads of the workgroup (wave scans
 // with shuffles, then the 16 wave totals through LDS).
 __device__ __forceinline__ int block_scan_incl(int x, int* wtot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  x = wave_scan_incl(x, lane);
   if (lane == 63) wtot[wave] = x;
   __syncthreads();
   int base = 0;
@@ -340,10 +366,11 @@ __device__ __forceinline__ int block_scan_incl(int x, int* wtot) {
 // workgroup of 1024 threads holds the masses in registers.
 template <int kTopkChunks>   // register capacity: kTopkChunks x 4096 keys
 __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectArgs a) {
+  constexpr int kSlots = kTopkChunks * kTopkWaves;   // (chunk, wave) pairs in index order
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kTkCopies * kTkStride];
   __shared__ int wtot[kTopkWaves];
-  __shared__ uint32_t hist[kTopkWaves][256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem, s_digit, s_above;
+  __shared__ int wsum[2][kSlots];
+  __shared__ int s_digit, s_above, s_eq;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv;
   const int ctx = clamp_ctx(a, b);
@@ -353,149 +380,215 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(SelectArgs a)
   const uint32_t* v = reinterpret_cast<const uint32_t*>(a.col_mass + static_cast<int64_t>(bh) * a.Tcap);
   int32_t* out = a.idx_out + static_cast<int64_t>(bh) * a.max_sel;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) {
-    s_prefix = 0;
-    s_krem = k;
-    a.n_out[bh] = k;
-  }
-  __syncthreads();
+  if (tid == 0) a.n_out[bh] = k;
   // The masses stay in registers for all passes: entry c*4096 + 4*tid + u
-  // in x[c][u].
+  // in x[c][u], read as one 16-byte load per lane for whole chunks.  Entries
+  // at or past n hold 0, the smallest pattern: with k <= n they never change
+  // the k-th largest, never exceed it, and come after every real entry in
+  // index order, so no pass or the compaction needs to test the index.
   uint32_t x[kTopkChunks][4];
   const int nch = (n + kTopkThreads * 4 - 1) / (kTopkThreads * 4);
+  const bool vec = (reinterpret_cast<uintptr_t>(v) & 15u) == 0;
 #pragma unroll
-  for (int c = 0; c < kTopkChunks; ++c)
+  for (int c = 0; c < kTopkChunks; ++c) {
+    const int i0 = c * kTopkThreads * 4 + tid * 4;
+    if (vec && (c + 1) * kTopkThreads * 4 <= n) {   // uniform
+      const uint4 w = *reinterpret_cast<const uint4*>(v + i0);
+      x[c][0] = w.x;
+      x[c][1] = w.y;
+      x[c][2] = w.z;
+      x[c][3] = w.w;
+    } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = c * kTopkThreads * 4 + tid * 4 + u;
-      x[c][u] = (c < nch && i < n) ? v[i] : 0u;
+      for (int u = 0; u < 4; ++u) x[c][u] = (c < nch && i0 + u < n) ? v[i0 + u] : 0u;
     }
+  }
   // Threshold: the k-th largest fp32 bit pattern tau (bit patterns of
   // non-negative values order like the values; any other pattern is ordered
   // as an unsigned integer, so exactly k entries are always taken).  Radix
-  // select, 8 bits per pass from the top: each pass counts, among the
-  // entries whose higher digits equal tau's, how many take each value of the
-  // next digit (wave-private LDS histograms), then takes the digit at which
-  // the count from the top reaches k.  `above` counts the entries already
-  // known to exceed tau.
-  uint32_t tau_bits = 0;
+  // select from the top: each pass counts, among the entries whose higher
+  // digits equal tau's, how many take each value of the next digit, then
+  // takes the digit at which the count from the top reaches k.  `above`
+  // counts the entries already known to exceed tau.
+  uint32_t tau = 0;
   int above = 0;
   if (k > 0) {
     uint32_t pmask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int e = tid; e < kTopkWaves * 256; e += kTopkThreads) hist[e >> 8][e & 255] = 0u;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int bits = pass == 0 ? kTkBits0 : kTkBits1;
+      const int shift = pass == 0 ? 32 - kTkBits0 : (pass == 1 ? 32 - kTkBits0 - kTkBits1 : 0);
+      const uint32_t dmask = (1u << bits) - 1u;
+      const int nb = 1 << bits;
+      // Clear the nb counters of every copy (16-byte words; kTkStride is a
+      // multiple of 4).
+      static_assert(kTkStride % 4 == 0, "counters are cleared as 16-byte words");
+      for (int e = tid; e < kTkCopies * nb / 4; e += kTopkThreads) {
+        const int cp = e / (nb / 4), w4 = e % (nb / 4);
+        reinterpret_cast<uint4*>(hist + cp * kTkStride)[w4] = uint4{0u, 0u, 0u, 0u};
+      }
       __syncthreads();
+      uint32_t* h = hist + (lane & (kTkCopies - 1)) * kTkStride;
+      if (pass == 0) {   // every entry counts
 #pragma unroll
-      for (int cc = 0; cc < kTopkChunks; ++cc) {
-        if (cc >= nch) break;
+        for (int c = 0; c < kTopkChunks; ++c) {
+          if (c >= nch) continue;   // uniform: every later chunk is empty too
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = cc * kTopkThreads * 4 + tid * 4 + u;
-          const bool on = i < n && (x[cc][u] & pmask) == tau_bits;
-          const uint32_t dg = (x[cc][u] >> shift) & 255u;
-          if (shift == 24) {
-            // The top digit (sign and high exponent bits) takes few distinct
-            // values, so most lanes of a wave would add to the same counter
-            // at once.  Lanes with equal digits are counted by ballot and one
-            // of them adds the count.
-            uint64_t act = __ballot(on);
-            while (act != 0ull) {
-              const int leader = __builtin_ctzll(act);
-              const uint32_t dl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dg), leader));
-              const uint64_t same = __ballot(on && dg == dl);
-              if (lane == leader) atomicAdd(&hist[wave][dl], static_cast<uint32_t>(__popcll(same)));
-              act &= ~same;
-            }
-          } else if (on) {
-            atomicAdd(&hist[wave][dg], 1u);
-          }
+          for (int u = 0; u < 4; ++u) atomicAdd(&h[x[c][u] >> shift], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < kTopkChunks; ++c) {
+          if (c >= nch) continue;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if ((x[c][u] & pmask) == tau) atomicAdd(&h[(x[c][u] >> shift) & dmask], 1u);
         }
       }
       __syncthreads();
-      // Thread t < 256 owns digit 255 - t, so its inclusive scan is the
-      // count of entries at or above that digit.
+      // Thread t owns the digits of descending rank t*bpt .. t*bpt + bpt - 1
+      // (digit nb - 1 - rank), so its inclusive scan counts the entries at
+      // or above its lowest digit.
+      const int bpt = nb / kTopkThreads;
       int cnt = 0;
-      if (tid < 256) {
-        for (int w = 0; w < kTopkWaves; ++w) cnt += static_cast<int>(hist[w][255 - tid]);
+      for (int j = 0; j < bpt; ++j) {
+        const int dg = nb - 1 - (tid * bpt + j);
+#pragma unroll
+        for (int cp = 0; cp < kTkCopies; ++cp) cnt += static_cast<int>(hist[cp * kTkStride + dg]);
       }
       const int incl = block_scan_incl(cnt, wtot);
-      if (tid < 256 && above + incl - cnt < k && above + incl >= k) {
-        s_digit = 255 - tid;
-        s_above = above + incl - cnt;
+      int acc = above + incl - cnt;
+      if (acc < k && above + incl >= k) {
+        for (int j = 0; j < bpt; ++j) {
+          const int dg = nb - 1 - (tid * bpt + j);
+          int cj = 0;
+#pragma unroll
+          for (int cp = 0; cp < kTkCopies; ++cp) cj += static_cast<int>(hist[cp * kTkStride + dg]);
+          if (acc + cj >= k) {
+            s_digit = dg;
+            s_above = acc;
+            s_eq = cj;   // after the last pass: the entries equal to tau
+            break;
+          }
+          acc += cj;
+        }
       }
       __syncthreads();
-      tau_bits |= static_cast<uint32_t>(s_digit) << shift;
-      pmask |= 255u << shift;
+      tau |= static_cast<uint32_t>(s_digit) << shift;
+      pmask |= dmask << shift;
       above = s_above;
-      __syncthreads();
-    }
-    if (tid == 0) {
-      s_prefix = tau_bits;
-      s_krem = k - above;
     }
   }
-  __syncthreads();
-  const uint32_t tau = s_prefix;
-  const int take_eq = s_krem;  // entries equal to the threshold to keep, lowest indices first
-  // Ordered compaction, chunk by chunk; ranks within a wave from ballots,
-  // across waves from the wave totals.
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int base_sel = 0, base_eq = 0;
+  // Ordered compaction in one scan.  Entries above tau are all taken; of the
+  // entries equal to tau the first take_eq in index order.  Index order is
+  // (chunk, wave, lane, u): in-wave prefixes by DPP scans, then the (chunk,
+  // wave) totals scanned by wave 0.  The indices go through LDS (the
+  // counters' space, free now) when they fit, so the global writes are whole
+  // rows instead of scattered words; entries not taken write to spare words
+  // past the staged indices.  Positions of taken entries are below k by
+  // construction; the test keeps every write inside the k-entry output all
+  // the same.
+  const int take_eq = k - above;
+  auto scan_slots = [&](int s) __attribute__((always_inline)) {
+    constexpr int F = kSlots / 64;   // slots per lane of wave 0
+    int val[F], tot = 0;
 #pragma unroll
-  for (int c = 0; c < kTopkChunks; ++c) {
-    if (c >= nch || k == 0) break;
-    const int c0 = c * kTopkThreads * 4;
-    bool gt[4], eq[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = c0 + tid * 4 + u;
-      gt[u] = i < n && x[c][u] > tau;
-      eq[u] = i < n && x[c][u] == tau;
+    for (int f = 0; f < F; ++f) {
+      val[f] = wsum[s][lane * F + f];
+      tot += val[f];
     }
-    // Rank of each equal entry among the equal entries (index order).
-    int eq_before = 0, eq_mine = 0;
+    int run = wave_scan_incl(tot, lane) - tot;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      eq_before += __popcll(__ballot(eq[u]) & lt);
-      eq_mine += eq[u] ? 1 : 0;
+    for (int f = 0; f < F; ++f) {
+      wsum[s][lane * F + f] = run;
+      run += val[f];
     }
-    if (lane == 63) wtot[wave] = eq_before + eq_mine;
+  };
+  int* stage = reinterpret_cast<int*>(hist);
+  static_assert(kTopkStage + 32 <= kTkCopies * kTkStride, "no spare words after the staged indices");
+  const int spare = kTopkStage + (lane & 31);
+  const bool staged = k <= kTopkStage;
+  if (k > 0 && s_eq == take_eq) {
+    // Every entry equal to tau is taken (no tie is cut): the taken entries
+    // are those at or above tau, one count per (chunk, thread).
+    int pre[kTopkChunks];
+#pragma unroll
+    for (int c = 0; c < kTopkChunks; ++c) {
+      int t = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t += x[c][u] >= tau ? 1 : 0;
+      const int incl = wave_scan_incl(t, lane);
+      pre[c] = incl - t;
+      if (lane == 63) wsum[0][c * kTopkWaves + wave] = incl;
+    }
     __syncthreads();
-    int eq_base = base_eq, eq_total = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      if (w < wave) eq_base += wtot[w];
-      eq_total += wtot[w];
-    }
+    if (wave == 0) scan_slots(0);
     __syncthreads();
-    bool sel[4];
-    int r_eq = eq_base + eq_before;
+    auto emit = [&](auto&& put) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sel[u] = gt[u];
-      if (eq[u]) {
-        sel[u] = r_eq < take_eq;
-        ++r_eq;
+      for (int c = 0; c < kTopkChunks; ++c) {
+        if (c >= nch) continue;   // uniform: every later chunk is empty too
+        int pos = wsum[0][c * kTopkWaves + wave] + pre[c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool keep = x[c][u] >= tau;
+          put(keep, pos, c * kTopkThreads * 4 + tid * 4 + u);
+          pos += keep ? 1 : 0;
+        }
+      }
+    };
+    if (staged) emit([&](bool keep, int pos, int i) { stage[keep && pos < k ? pos : spare] = i; });
+    else emit([&](bool keep, int pos, int i) { if (keep && pos < k) out[pos] = i; });
+  } else if (k > 0) {
+    // Ties at tau are cut: an entry's position is (entries above tau before
+    // it) + min(entries equal to tau before it, take_eq), the two counts
+    // packed in one word for the in-wave scan (each at most 256 per wave and
+    // chunk).
+    int pre[kTopkChunks];
+#pragma unroll
+    for (int c = 0; c < kTopkChunks; ++c) {
+      int g = 0, e = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        g += x[c][u] > tau ? 1 : 0;
+        e += x[c][u] == tau ? 1 : 0;
+      }
+      const int own = g | (e << 16);
+      const int incl = wave_scan_incl(own, lane);
+      pre[c] = incl - own;
+      if (lane == 63) {
+        wsum[0][c * kTopkWaves + wave] = incl & 0xFFFF;
+        wsum[1][c * kTopkWaves + wave] = incl >> 16;
       }
     }
-    int sel_before = 0, sel_mine = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sel_before += __popcll(__ballot(sel[u]) & lt);
-      sel_mine += sel[u] ? 1 : 0;
-    }
-    if (lane == 63) wtot[wave] = sel_before + sel_mine;
     __syncthreads();
-    int pos = base_sel + sel_before, sel_total = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      if (w < wave) pos += wtot[w];
-      sel_total += wtot[w];
+    if (wave == 0) {
+      scan_slots(0);
+      scan_slots(1);
     }
     __syncthreads();
+    auto emit = [&](auto&& put) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (sel[u]) out[pos++] = c0 + tid * 4 + u;
-    base_sel += sel_total;
-    base_eq += eq_total;
+      for (int c = 0; c < kTopkChunks; ++c) {
+        if (c >= nch) continue;   // uniform: every later chunk is empty too
+        int g = wsum[0][c * kTopkWaves + wave] + (pre[c] & 0xFFFF);
+        int e = wsum[1][c * kTopkWaves + wave] + (pre[c] >> 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool gt = x[c][u] > tau, eq = x[c][u] == tau;
+          const int ecl = e < take_eq ? e : take_eq;
+          put(gt || (eq && e < take_eq), g + (gt ? ecl : e), c * kTopkThreads * 4 + tid * 4 + u);
+          g += gt ? 1 : 0;
+          e += eq ? 1 : 0;
+        }
+      }
+    };
+    if (staged) emit([&](bool keep, int pos, int i) { stage[keep && pos < k ? pos : spare] = i; });
+    else emit([&](bool keep, int pos, int i) { if (keep && pos < k) out[pos] = i; });
+  }
+  if (k > 0 && staged) {
+    __syncthreads();
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = stage[i];
   }
   for (int i = k + tid; i < a.max_sel; i += kTopkThreads) out[i] = -1;
 }
@@ -507,17 +600,23 @@ hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream) {
     const dim3 g1(nchunk, a.B * a.Hkv);
     const int nq = a.B * a.Hkv * G * a.R;
     const dim3 g3((a.Tcap + kCmKeys - 1) / kCmKeys, a.B * a.Hkv);
+    // Up to 256 recent queries x group size: the 8-group instances; the
+    // host caps the count at kMaxRecent, which the 16-group ones hold.
+    static_assert(kMaxRecent <= 16 * 32, "recent queries beyond the largest instance");
+    const bool small = G * a.R <= 8 * 32;
+    void (*stats)(SelectArgs) = nullptr;
+    void (*colmass)(SelectArgs) = nullptr;
     if (D == 128) {
-      hipLaunchKernelGGL(select_stats_kernel<128>, g1, dim3(kSelThreads), 0, stream, a);
-      hipLaunchKernelGGL(select_finalize_kernel, dim3((nq + kSelThreads - 1) / kSelThreads), dim3(kSelThreads), 0,
-                         stream, a);
-      hipLaunchKernelGGL(select_colmass_kernel<128>, g3, dim3(kSelThreads), 0, stream, a);
+      stats = small ? select_stats_kernel<128, 8> : select_stats_kernel<128, 16>;
+      colmass = small ? select_colmass_kernel<128, 8> : select_colmass_kernel<128, 16>;
     } else {
-      hipLaunchKernelGGL(select_stats_kernel<64>, g1, dim3(kSelThreads), 0, stream, a);
-      hipLaunchKernelGGL(select_finalize_kernel, dim3((nq + kSelThreads - 1) / kSelThreads), dim3(kSelThreads), 0,
-                         stream, a);
-      hipLaunchKernelGGL(select_colmass_kernel<64>, g3, dim3(kSelThreads), 0, stream, a);
+      stats = small ? select_stats_kernel<64, 8> : select_stats_kernel<64, 16>;
+      colmass = small ? select_colmass_kernel<64, 8> : select_colmass_kernel<64, 16>;
     }
+    hipLaunchKernelGGL(stats, g1, dim3(kSelThreads), 0, stream, a);
+    hipLaunchKernelGGL(select_finalize_kernel, dim3((nq + kSelThreads - 1) / kSelThreads), dim3(kSelThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL(colmass, g3, dim3(kSelThreads), 0, stream, a);
   }
   // Contexts up to 32K keep 32 masses per thread in registers; longer ones
   // (up to 64K) hold 64, part of them spilled.

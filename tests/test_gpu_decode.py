@@ -450,6 +450,34 @@ def test_topk_exact_on_edge_masses(kind):
             assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
 
 
+@pytest.mark.parametrize("kind", ["uniform", "ties"])
+def test_topk_exact_large_k_and_unaligned_rows(kind):
+    """R = 0, top-k only, indices equal to the oracle's: a 64K context with
+    rho = 60% selects more than 32768 keys, past what the kernel stages in
+    LDS, so the indices are written straight to the output; the mass rows
+    are 16-byte misaligned (Tcap odd), which takes the word-wise loads."""
+    rng = np.random.default_rng(47)
+    b, hkv, tcap = 2, 2, 65533
+    if kind == "uniform":
+        cm = rng.uniform(0, 3, size=(b, hkv, tcap)).astype(np.float32)
+    else:
+        cm = rng.integers(0, 6, size=(b, hkv, tcap)).astype(np.float32)
+    ctx = np.array([tcap, 40001], dtype=np.int32)
+    kc = mxa.empty_mx((b, hkv, tcap, 64), "hd", DEV)
+    col = torch.from_numpy(cm).to(DEV)
+    print(f"top-k large k {kind}", flush=True)
+    idx, n = mxa.select_vertical(None, kc, torch.from_numpy(ctx).to(DEV), col, window=100,
+                                 rho_num=60, rho_den=100)
+    torch.cuda.synchronize()
+    assert int(n[0, 0]) > 32768
+    for bb in range(b):
+        for h in range(hkv):
+            want = select.topk_vertical(cm[bb, h], int(ctx[bb]), 100, 60, 100)
+            got = idx[bb, h, : int(n[bb, h])].cpu().numpy()
+            np.testing.assert_array_equal(got, want, err_msg=f"{kind} b{bb} h{h}")
+            assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
+
+
 def test_select_vertical_32k_batch8():
     """col_mass from 64 recent queries x 4 heads per KV head over ctx 32768,
     then the top 5% of the non-window prefix; two calls accumulate."""
