@@ -30,8 +30,11 @@ COMMON = [
 
 
 # Per-source additions.  The attention kernel's logits are finite or -inf
-# (masked keys) and never NaN, so max/min need no NaN canonicalisation.
-EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# (masked keys) and never NaN, so max/min need no NaN canonicalisation.  The
+# selection kernels keep their MFMA results in VGPRs: with accumulators in
+# AGPRs the column-mass loop copied every logit out before its exponential.
+EXTRA = {"prefill.hip": ["-fno-honor-nans"],
+         "select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc():

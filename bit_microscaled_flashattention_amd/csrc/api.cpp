@@ -566,7 +566,9 @@ mxattn_status_t mxattn_decode_paged(const mxattn_mx_t* q, const mxattn_mx_t* q_r
 }
 
 // Per (batch, query head, recent query, context chunk): partial (max, sum)
-// of the logits; chunk = kSelectChunk keys.
+// of the logits, then one slot for their merge; chunk = kSelectChunk keys,
+// so a context of at most 65536 keys has at most 32 chunks (the merge reads
+// that many at once).
 static constexpr int64_t kSelectChunk = 2048;
 
 size_t mxattn_select_workspace_bytes(int64_t batch, int64_t hq, int64_t recent, int64_t tcap) {

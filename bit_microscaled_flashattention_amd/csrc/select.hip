@@ -59,6 +59,7 @@ __device__ __forceinline__ float* stat_slot(const SelectArgs& a, int b, int hk, 
 
 // ---------------------------------------------------------------------------
 constexpr int kMaxRecent = 512;    // recent queries x group size held in LDS
+constexpr int kMaxChunks = 32;     // context chunks (Tcap <= 65536, 2048-key chunks)
 
 // The group's recent queries in LDS: codes [nq][D/2] and scales [nq][D/32].
 // Queries past nq up to the next multiple of 32 are zero codes with scale
@@ -219,7 +220,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs
   }
 }
 
-// Ordered merge of the chunk partials of every recent query.
+// Ordered merge of the chunk partials of every recent query into the slot
+// after them.  Every partial is read at once (at most kMaxChunks of them):
+// a loop of dependent reads cost one memory latency per chunk.
 __global__ __launch_bounds__(kSelThreads) void select_finalize_kernel(SelectArgs a) {
   const int G = a.Hq / a.Hkv;
   const int nq = a.B * a.Hkv * G * a.R;
@@ -230,13 +233,18 @@ __global__ __launch_bounds__(kSelThreads) void select_finalize_kernel(SelectArgs
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int nchunk = (a.Tcap + a.chunk - 1) / a.chunk;
   const int used = (clamp_ctx(a, b) + a.chunk - 1) / a.chunk;
+  float2 st[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    st[c] = c < used ? *reinterpret_cast<const float2*>(stat_slot(a, b, hk, qi, c))
+                     : make_float2(-__builtin_huge_valf(), 0.0f);
   float M = -__builtin_huge_valf();
-  for (int c = 0; c < used; ++c) M = fmaxf(M, stat_slot(a, b, hk, qi, c)[0]);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, st[c].x);
   float L = 0.0f;
-  for (int c = 0; c < used; ++c) {
-    const float* st = stat_slot(a, b, hk, qi, c);
-    if (st[0] != -__builtin_huge_valf()) L += fast_exp2((st[0] - M) * a.c) * st[1];
-  }
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    if (st[c].x != -__builtin_huge_valf()) L += fast_exp2((st[c].x - M) * a.c) * st[c].y;
   float* out = stat_slot(a, b, hk, qi, nchunk);
   out[0] = M;
   out[1] = 1.0f / L;
