@@ -566,14 +566,28 @@ mxattn_status_t mxattn_decode_paged(const mxattn_mx_t* q, const mxattn_mx_t* q_r
 }
 
 // Per (batch, query head, recent query, context chunk): partial (max, sum)
-// of the logits, then one slot for their merge; chunk = kSelectChunk keys,
-// so a context of at most 65536 keys has at most 32 chunks (the merge reads
-// that many at once).
-static constexpr int64_t kSelectChunk = 2048;
+// of the logits, then one slot for their merge.  Chunks are 2048 keys when
+// the batch gives the stats kernel at least 128 chunks per KV head, shorter
+// (down to 256) for short contexts so that their few workgroups still spread
+// over the CUs; never more than 32 chunks (the merge reads that many at once).
+static int64_t select_chunk(int64_t batch, int64_t tcap) {
+  int64_t chunk = 2048;
+  while (chunk > 256 && batch * ((tcap + chunk - 1) / chunk) < 128) chunk /= 2;
+  while ((tcap + chunk - 1) / chunk > 32) chunk *= 2;
+  return chunk;
+}
+
+// Keys per column-mass workgroup: 512, down to 128 for short contexts.
+static int select_cm_keys(int64_t batch, int64_t tcap) {
+  int keys = 512;
+  while (keys > 128 && batch * ((tcap + keys - 1) / keys) < 256) keys /= 2;
+  return keys;
+}
 
 size_t mxattn_select_workspace_bytes(int64_t batch, int64_t hq, int64_t recent, int64_t tcap) {
   if (batch < 1 || hq < 1 || recent < 0 || tcap < 1) return 0;
-  const int64_t nchunk = (tcap + kSelectChunk - 1) / kSelectChunk;
+  const int64_t chunk = select_chunk(batch, tcap);
+  const int64_t nchunk = (tcap + chunk - 1) / chunk;
   const int64_t n = batch * hq * (recent > 0 ? recent : 1) * (nchunk + 1) * 2;
   return static_cast<size_t>(n) * sizeof(float);
 }
@@ -608,7 +622,8 @@ mxattn_status_t mxattn_select_vertical(const mxattn_mx_t* q, const mxattn_mx_t* 
   if (!aligned16(workspace)) return fail(MXATTN_ERR_INVALID_ARG, "select: workspace not 16-byte aligned");
   SelectArgs a{};
   a.stats = static_cast<float*>(workspace);
-  a.chunk = static_cast<int>(kSelectChunk);
+  a.chunk = static_cast<int>(select_chunk(kc->batch, kc->seq));
+  a.cm_keys = select_cm_keys(kc->batch, kc->seq);
   if (q) a.q = view_of(q);
   a.k = view_of(kc);
   a.ctx_len = ctx_len;

@@ -142,7 +142,8 @@ struct SelectArgs {
   int window, rho_num, rho_den, max_sel;
   float* col_mass;
   float* stats;         // [B][Hq][R][nchunk+1][2] partial row max / sum (workspace)
-  int chunk;            // keys per context chunk
+  int chunk;            // keys per context chunk of the stats kernel (multiple of 128)
+  int cm_keys;          // keys per column-mass workgroup (multiple of 128)
   int32_t* idx_out;
   int32_t* n_out;
 };

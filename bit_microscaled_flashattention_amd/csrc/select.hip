@@ -6,11 +6,11 @@
 // rho fraction of highest-scoring keys before the recent window.
 //
 // Kernels
-//   stats    -- per (2048-key context chunk, batch x KV head): every recent
+//   stats    -- per (context chunk, batch x KV head): every recent
 //               query's partial row max and row sum of the logits (S^T =
 //               K_hat q_hat^T on the scaled FP4 MFMA, queries staged in
 //               LDS), merged per query in chunk order by `finalize`.
-//   colmass  -- per 512-key block: the normalised probabilities of every
+//   colmass  -- per key block: the normalised probabilities of every
 //               recent query of the KV head's group, summed per key (in-lane
 //               over 16 queries, a permlane32 swap for the other 16) and added
 //               to col_mass.  Each key belongs to exactly one lane: no atomics.
@@ -59,7 +59,7 @@ __device__ __forceinline__ float* stat_slot(const SelectArgs& a, int b, int hk, 
 
 // ---------------------------------------------------------------------------
 constexpr int kMaxRecent = 512;    // recent queries x group size held in LDS
-constexpr int kMaxChunks = 32;     // context chunks (Tcap <= 65536, 2048-key chunks)
+constexpr int kMaxChunks = 32;     // context chunks (the host sizes chunks to stay within it)
 
 // The group's recent queries in LDS: codes [nq][D/2] and scales [nq][D/32].
 // Queries past nq up to the next multiple of 32 are zero codes with scale
@@ -251,12 +251,11 @@ __global__ __launch_bounds__(kSelThreads) void select_finalize_kernel(SelectArgs
 }
 
 // ---------------------------------------------------------------------------
-// Per (512-key block, batch x KV head): the normalised probabilities of
-// every recent query of the group, summed per key and added to col_mass.
-// Lane (key j, half hh) of a 32x32 product holds 16 queries, in four runs of
-// four consecutive ones, so their (m c, 1/l) come from LDS as float4s.  Each
-// key belongs to one lane pair: no atomics.
-constexpr int kCmKeys = 512;
+// Per (block of cm_keys keys, batch x KV head): the normalised
+// probabilities of every recent query of the group, summed per key and added
+// to col_mass.  Lane (key j, half hh) of a 32x32 product holds 16 queries, in
+// four runs of four consecutive ones, so their (m c, 1/l) come from LDS as
+// float4s.  Each key belongs to one lane pair: no atomics.
 
 template <int D, int NG>
 __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs a) {
@@ -269,9 +268,9 @@ __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs 
   const int nq = G * a.R, ng = (nq + 31) / 32;
   const int nchunk = (a.Tcap + a.chunk - 1) / a.chunk;
   const int ctx = clamp_ctx(a, b);
-  const int k_lo = blk * kCmKeys;
+  const int k_lo = blk * a.cm_keys;
   if (k_lo >= ctx) return;
-  const int k_hi = min(k_lo + kCmKeys, ctx);
+  const int k_hi = min(k_lo + a.cm_keys, ctx);
   stage_queries<D>(a, b, hk, q_lds, qs_lds);
   for (int qi = threadIdx.x; qi < ng * 32; qi += kSelThreads) {
     float mcv = 0.0f, il = 0.0f;   // padding queries contribute 0
@@ -607,7 +606,7 @@ hipError_t launch_select(const SelectArgs& a, int D, hipStream_t stream) {
     const int nchunk = (a.Tcap + a.chunk - 1) / a.chunk;
     const dim3 g1(nchunk, a.B * a.Hkv);
     const int nq = a.B * a.Hkv * G * a.R;
-    const dim3 g3((a.Tcap + kCmKeys - 1) / kCmKeys, a.B * a.Hkv);
+    const dim3 g3((a.Tcap + a.cm_keys - 1) / a.cm_keys, a.B * a.Hkv);
     // Up to 256 recent queries x group size: the 8-group instances; the
     // host caps the count at kMaxRecent, which the 16-group ones hold.
     static_assert(kMaxRecent <= 16 * 32, "recent queries beyond the largest instance");
