@@ -254,14 +254,15 @@ __global__ __launch_bounds__(kSelThreads) void select_finalize_kernel(SelectArgs
 // Per (block of cm_keys keys, batch x KV head): the normalised
 // probabilities of every recent query of the group, summed per key and added
 // to col_mass.  Lane (key j, half hh) of a 32x32 product holds 16 queries, in
-// four runs of four consecutive ones, so their (m c, 1/l) come from LDS as
-// float4s.  Each key belongs to one lane pair: no atomics.
+// four runs of four consecutive ones, so their offsets w = m c + log2 l come
+// from LDS as float4s (exp2(s c - w) = exp2(s c - m c) / l: one LDS word per
+// query instead of two).  Each key belongs to one lane pair: no atomics.
 
 template <int D, int NG>
 __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[NG * 32 * (D / 2)];
   __shared__ uint8_t qs_lds[NG * 32 * (D / 32)];
-  __shared__ __attribute__((aligned(16))) float mc_lds[NG * 32], il_lds[NG * 32];
+  __shared__ __attribute__((aligned(16))) float w_lds[NG * 32];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int G = a.Hq / a.Hkv;
@@ -273,14 +274,12 @@ __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs 
   const int k_hi = min(k_lo + a.cm_keys, ctx);
   stage_queries<D>(a, b, hk, q_lds, qs_lds);
   for (int qi = threadIdx.x; qi < ng * 32; qi += kSelThreads) {
-    float mcv = 0.0f, il = 0.0f;   // padding queries contribute 0
+    float w = __builtin_huge_valf();   // padding queries contribute exp2(-inf) = 0
     if (qi < nq) {
       const float* st = stat_slot(a, b, hk, qi, nchunk);
-      mcv = st[0] * a.c;
-      il = st[1];
+      w = st[0] * a.c - log2f(st[1]);   // st[1] = 1 / l
     }
-    mc_lds[qi] = mcv;
-    il_lds[qi] = il;
+    w_lds[qi] = w;
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 31, hh = lane >> 5;
@@ -312,11 +311,9 @@ __global__ __launch_bounds__(kSelThreads) void select_colmass_kernel(SelectArgs 
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int qb = g * 32 + 8 * q4 + 4 * hh;
-        const v4f mcv = *reinterpret_cast<const v4f*>(mc_lds + qb);
-        const v4f ilv = *reinterpret_cast<const v4f*>(il_lds + qb);
+        const v4f wv = *reinterpret_cast<const v4f*>(w_lds + qb);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          colsum = __builtin_fmaf(fast_exp2(__builtin_fmaf(s[4 * q4 + r], a.c, -mcv[r])), ilv[r], colsum);
+        for (int r = 0; r < 4; ++r) colsum += fast_exp2(__builtin_fmaf(s[4 * q4 + r], a.c, -wv[r]));
       }
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(colsum), __float_as_uint(colsum), false, false);
