@@ -148,6 +148,22 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs
     m[g] = -__builtin_huge_valf();
     l[g] = 0.0f;
   }
+  // Up to 16 query operands (8 groups at D = 128) stay in registers for the
+  // whole chunk instead of being read from LDS for every key block: 92 ->
+  // 89 us on the 32K batch-8 selection; 16 groups at D = 128 would spill.
+  constexpr bool kQReg = NG * (D / 64) <= 16;
+  v4i qreg[kQReg ? NG : 1][D / 64];
+  int qsreg[kQReg ? NG : 1][D / 64];
+  if constexpr (kQReg) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int dc = 0; dc < D / 64; ++dc) {
+        const int qi = g * 32 + j;
+        qreg[g][dc] = *reinterpret_cast<const v4i*>(q_lds + qi * (D / 2) + dc * 32 + hh * 16);
+        qsreg[g][dc] = qs_lds[qi * (D / 32) + 2 * dc + hh];
+      }
+  }
   int t0 = t_lo + wave * 32;
   KBlock<D> kn = load_kblock<D>(rc, rs, kcs, kss, t0 + j, t_hi, hh);
   for (; t0 < t_hi; t0 += 128) {
@@ -160,14 +176,18 @@ __global__ __launch_bounds__(kSelThreads, 2) void select_stats_kernel(SelectArgs
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g >= ng) continue;   // uniform; the loop stays unrolled, m[g]/l[g] in fixed registers
-        // B operand: query g*32 + j from LDS.
+        // B operand: query g*32 + j, from registers or LDS.
         const int qi = g * 32 + j;
         v16f s = v16f{};
 #pragma unroll
         for (int dc = 0; dc < D / 64; ++dc) {
-          const v4i qop = *reinterpret_cast<const v4i*>(q_lds + qi * (D / 2) + dc * 32 + hh * 16);
-          const int qsc = qs_lds[qi * (D / 32) + 2 * dc + hh];
-          s = mfma32_fp4(kb.op[dc], qop, s, kb.sc[dc], qsc);
+          if constexpr (kQReg) {
+            s = mfma32_fp4(kb.op[dc], qreg[g][dc], s, kb.sc[dc], qsreg[g][dc]);
+          } else {
+            const v4i qop = *reinterpret_cast<const v4i*>(q_lds + qi * (D / 2) + dc * 32 + hh * 16);
+            const int qsc = qs_lds[qi * (D / 32) + 2 * dc + hh];
+            s = mfma32_fp4(kb.op[dc], qop, s, kb.sc[dc], qsc);
+          }
         }
         // Lane (query j, half hh) holds keys t0 + 8(r/4) + 4hh + r%4.
         if constexpr (TAIL) {
