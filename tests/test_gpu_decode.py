@@ -478,6 +478,38 @@ def test_topk_exact_large_k_and_unaligned_rows(kind):
             assert (idx[bb, h, int(n[bb, h]):].cpu().numpy() == -1).all()
 
 
+@pytest.mark.parametrize("b,hq,hkv,r,d,tcap,ctxs", [
+    (2, 8, 1, 40, 64, 3000, (3000, 1777)),   # 320 queries: 16-group state, operands read from LDS
+    (1, 4, 2, 17, 128, 9000, (8999,)),       # 34 queries: partial groups, operands in registers
+    (3, 4, 1, 64, 128, 1100, (1100, 129, 700)),
+])
+def test_select_column_mass_short_contexts(b, hq, hkv, r, d, tcap, ctxs):
+    """Column mass and top 5% against the oracle where the stats chunks and
+    column-mass blocks shrink for short contexts (256-512-key chunks,
+    128-key blocks), on ragged contexts, with 16 query groups, partial
+    groups and D = 64."""
+    g = torch.Generator(device=DEV).manual_seed(1000 + tcap)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    q = torch.randn((b, hq, r, d), generator=g, device=DEV).to(torch.bfloat16)
+    kc, qr = mxa.quantize(k, "hd"), mxa.quantize(q, "hd")
+    ctx = torch.tensor(ctxs, dtype=torch.int32, device=DEV)
+    col = torch.zeros((b, hkv, tcap), dtype=torch.float32, device=DEV)
+    print(f"select short contexts b={b} hq={hq} hkv={hkv} r={r} d={d} tcap={tcap}", flush=True)
+    idx, n = mxa.select_vertical(qr, kc, ctx, col, window=32)
+    torch.cuda.synchronize()
+    kd = oracle_dequant(*oracle_quantize(host_f64(k), "hd"), "hd")
+    qd = oracle_dequant(*oracle_quantize(host_f64(q), "hd"), "hd")
+    grp = hq // hkv
+    for bb in range(b):
+        c = int(ctxs[bb])
+        for h in range(hkv):
+            ocm = select.colmass_update(np.zeros(tcap), qd[bb, grp * h:grp * (h + 1)].reshape(-1, d), kd[bb, h], c)
+            np.testing.assert_allclose(col[bb, h].cpu().numpy(), ocm, rtol=2e-4, atol=1e-7,
+                                       err_msg=f"column mass b{bb} h{h}")
+            check_selection(idx[bb, h, : int(n[bb, h])].cpu().numpy(), int(n[bb, h]), ocm, c, 32, 5, 100,
+                            f"select b{bb} h{h}")
+
+
 def test_select_vertical_32k_batch8():
     """col_mass from 64 recent queries x 4 heads per KV head over ctx 32768,
     then the top 5% of the non-window prefix; two calls accumulate."""
