@@ -47,23 +47,26 @@ HYBRID_WINDOW = 128     # bf16 recent window (decode and hybrid prefill)
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # 4K causal GQA step: fetch 6840.69 KiB x 2.000 + write 65579.34 KiB x 1.000 per dispatch (medians)
-    "prefill_kernel<128,128,true,true>": {"bytes": 81162976, "sources": "875cbd3269e8a052"},
-    # 32K non-causal UOS (24 heads): fetch 1267412.4 KiB x 2 + write 393218.0 KiB (median of 8): K/V of a
+    # 4K causal GQA step: fetch 6831.63 KiB x 2.000 + write 65577.20 KiB x 1.000 per dispatch (medians)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81142224, "sources": "33fdff6f61e3f02b"},
+    # 32K non-causal UOS (24 heads): fetch 1267416.4 KiB x 2 + write 393219.2 KiB (median of 8): K/V of a
     # head re-read from the memory side by each of its 256 query blocks (three heads per XCD exceed its L2)
-    "prefill_kernel<128,128,false,true> uos": {"bytes": 2998315952, "sources": "875cbd3269e8a052"},
-    # 32K batch-32 call (bf16 query encoded in the scan): scan fetch 557308 KiB x 2 + write 1088 KiB
-    # (median of 8), plus the merge (1750016 bytes)
-    "decode_scan_kernel<128> split 16384": {"bytes": 1144272000, "sources": "df608f45c739eb73"},
-    # 32K batch-8 hybrid call: scan 347713600 bytes (median of 8) + merge 2307072; the 4-bit rows of the
-    # bf16-held tokens are not fetched, but their 128-byte lines mostly hold a neighbour that is
-    "decode_scan_kernel<128> hybrid split 2752": {"bytes": 350020672, "sources": "df608f45c739eb73"},
+    "prefill_kernel<128,128,false,true> uos": {"bytes": 2998325200, "sources": "33fdff6f61e3f02b"},
+    # 32K batch-32 call (bf16 query encoded in the scan): scan fetch 557328.2 KiB x 2 + write 1088 KiB
+    # (median of 8), plus the merge (fetch 598.5 KiB x 2 + write 512 KiB)
+    "decode_scan_kernel<128> split 16384": {"bytes": 1144272192, "sources": "beacda9caff5c1c1"},
+    # 32K batch-8 hybrid call: scan fetch 168693.8 KiB x 2 + write 2176.5 KiB (median of 8) + merge
+    # 2307072; the 4-bit rows of the bf16-held tokens are not fetched, but their 128-byte lines mostly
+    # hold a neighbour that is
+    "decode_scan_kernel<128> hybrid split 2752": {"bytes": 350020688, "sources": "beacda9caff5c1c1"},
 }
 TRAFFIC_SOURCES = {
     "prefill": ["bit_microscaled_flashattention_amd/csrc/prefill.hip",
-                "bit_microscaled_flashattention_amd/csrc/mx_device.h"],
+                "bit_microscaled_flashattention_amd/csrc/mx_device.h",
+                "bit_microscaled_flashattention_amd/csrc/kernels.h"],
     "decode": ["bit_microscaled_flashattention_amd/csrc/decode.hip",
-               "bit_microscaled_flashattention_amd/csrc/mx_device.h"],
+               "bit_microscaled_flashattention_amd/csrc/mx_device.h",
+               "bit_microscaled_flashattention_amd/csrc/kernels.h"],
 }
 
 
