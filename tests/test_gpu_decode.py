@@ -347,6 +347,29 @@ def test_hybrid_decode_small(window, n_sel):
         assert (plain - out).abs().max().item() < 1e-5
 
 
+def test_decode_at_the_slot_limit():
+    """The largest number of partial slots a call accepts (4096 per sequence:
+    a 262144-token cache in splits of 64) against the oracle, with a ragged
+    context that leaves the last 13 tokens out; one slot more is refused
+    before launch."""
+    g = torch.Generator(device=DEV).manual_seed(36)
+    b, hq, hkv, tcap, d, split = 1, 4, 1, 4096 * 64, 64, 64
+    q = torch.randn((b, hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((b, hkv, tcap, d), generator=g, device=DEV).to(torch.bfloat16)
+    ctx = torch.tensor([tcap - 13], dtype=torch.int32, device=DEV)
+    print("decode: 4096 slots of 64 tokens", flush=True)
+    kc, vc = _cache(k, v)
+    out, lse = mxa.decode(_query(q), kc, vc, ctx, split_len=split, return_lse=True)
+    torch.cuda.synchronize()
+    ref = _oracle_pair(q, k, v, ctx.cpu().numpy(), [(0, h) for h in range(hq)])
+    _compare(out, lse, ref, "4096 slots")
+    k2 = torch.zeros((b, hkv, tcap + 64, d), dtype=torch.bfloat16, device=DEV)
+    kc2 = mxa.quantize(k2, "hd")
+    with pytest.raises(mxa.MxattnError, match="partial slots"):
+        mxa.decode(_query(q), kc2, kc2, ctx, split_len=split)
+
+
 def test_decode_32k_batch32_full_size():
     """Batch 32, 32/8 heads, D=128, ctx 32768, split 2048: cache codes of the
     sampled KV heads bit-exact, 12 sampled (b, hq) outputs vs the oracle."""
