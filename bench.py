@@ -47,11 +47,11 @@ HYBRID_WINDOW = 128     # bf16 recent window (decode and hybrid prefill)
 # A figure is reported only while the kernel's sources hash to the profiled
 # state; after any change to them it is null until profiled again.
 PROFILED_TRAFFIC = {
-    # 4K causal GQA step: fetch 6831.63 KiB x 2.000 + write 65577.20 KiB x 1.000 per dispatch (medians)
-    "prefill_kernel<128,128,true,true>": {"bytes": 81142224, "sources": "33fdff6f61e3f02b"},
-    # 32K non-causal UOS (24 heads): fetch 1267416.4 KiB x 2 + write 393219.2 KiB (median of 8): K/V of a
-    # head re-read from the memory side by each of its 256 query blocks (three heads per XCD exceed its L2)
-    "prefill_kernel<128,128,false,true> uos": {"bytes": 2998325200, "sources": "33fdff6f61e3f02b"},
+    # 4K causal GQA step: fetch 6841.09 KiB x 2.000 + write 65572.91 KiB x 1.000 per dispatch (medians)
+    "prefill_kernel<128,128,true,true>": {"bytes": 81157216, "sources": "01d8c7ff8dd1bf2f"},
+    # 32K non-causal UOS (24 heads): fetch 429522.97 KiB x 2 + write 393216.0 KiB (median of 8); each XCD
+    # runs one head's query blocks after another, whose K/V (4.46 MB) slightly exceed its 4 MB L2
+    "prefill_kernel<128,128,false,true> uos": {"bytes": 1282316224, "sources": "01d8c7ff8dd1bf2f"},
     # 32K batch-32 call (bf16 query encoded in the scan): scan fetch 557328.2 KiB x 2 + write 1088 KiB
     # (median of 8), plus the merge (fetch 598.5 KiB x 2 + write 512 KiB)
     "decode_scan_kernel<128> split 16384": {"bytes": 1144272192, "sources": "beacda9caff5c1c1"},

@@ -234,7 +234,12 @@ __device__ __forceinline__ float p_block_scale(float pmax, bool uos, int thr) {
 // Workgroup -> (query block, batch, query head).  Consecutive workgroups go
 // to different XCDs (round robin over 8); the mapping gives each XCD whole
 // (batch, KV head) pairs so their K/V stay in that XCD's L2, and issues the
-// longest causal query blocks first.
+// longest causal query blocks first.  Without a causal mask every block is
+// equally long, and an XCD runs the blocks of one (batch, KV head) pair
+// after another (query block fastest): its resident workgroups then share
+// one pair's K/V in L2, where with the pairs interleaved each block read
+// its pair's K/V again from beyond the L2 once the XCD's pairs together
+// outgrew it.
 __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int& qb, int& b, int& hq) {
   const int G = a.Hq / a.Hkv;
   const int pairs = a.B * a.Hkv;
@@ -243,10 +248,17 @@ __device__ __forceinline__ void map_block(const PrefillArgs& a, bool causal, int
   if (pairs % 8 == 0) {
     const int slot = bid % 8, rank = bid / 8;
     const int per = pairs / 8;
-    qi = rank / (per * G);
-    const int rem = rank % (per * G);
-    pair = slot * per + rem / G;
-    g = rem % G;
+    if (causal) {
+      qi = rank / (per * G);
+      const int rem = rank % (per * G);
+      pair = slot * per + rem / G;
+      g = rem % G;
+    } else {
+      qi = rank % a.n_qblk;
+      const int rem = rank / a.n_qblk;
+      pair = slot * per + rem / G;
+      g = rem % G;
+    }
   } else {
     qi = bid / (pairs * G);
     const int rem = bid % (pairs * G);
