@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mx
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mxattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mxattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
