@@ -94,7 +94,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="prefill,diffusion,decode,hybrid,tiny",
-                    help="comma list of legs to run (prefill is the headline)")
+                    help="comma list of legs to run (prefill is the headline); 'quant' (alone or with "
+                         "other non-prefill legs) launches the 4K step's quantiser jobs one at a time")
     ap.add_argument("--kv-tile", type=int, default=KV_TILE)
     ap.add_argument("--decode-split", type=int, default=DECODE_SPLIT, help="tokens per split, 32K decode leg")
     ap.add_argument("--hybrid-split", type=int, default=HYBRID_SPLIT, help="tokens per split, hybrid decode leg")
@@ -171,6 +172,30 @@ def launch_events(kernel_fn, n):
 
 
 # ------------------------------------------------------------------ prefill
+def quant_jobs_leg(args):
+    """The 4K step's three quantiser jobs one at a time (Q and K in head-dim
+    blocks with their Smooth-QK factors, V in key blocks), `steps` launches of
+    each in that order, for per-job counter and trace runs."""
+    import torch
+    import bit_microscaled_flashattention_amd as mxa
+    import synth
+
+    B, HQ, HKV, S, D = 1, 32, 8, 4096, 128
+    d = synth.gqa_prefill(device="cuda")
+    qs, ks = mxa.smooth_calibrate(d["q_cal"], d["k_cal"])
+    jobs = {"q_hd": dict(x=d["q"], chan_scale=qs, out=mxa.empty_mx((B, HQ, S, D), "hd")),
+            "k_hd": dict(x=d["k"], chan_scale=ks, out=mxa.empty_mx((B, HKV, S, D), "hd")),
+            "v_key": dict(x=d["v"], layout="key", out=mxa.empty_mx((B, HKV, S, D), "key"))}
+    settle_clocks(lambda: mxa.quantize_batch(list(jobs.values())))
+    res = {}
+    for name, job in jobs.items():
+        _, t = timed(lambda: None, args.steps, 0, lambda job=job: mxa.quantize_batch([job]))
+        res[name] = {"ms": round(t * 1e3, 4)}
+    res["note"] = ("the 4K step's quantiser jobs launched alone, in this order; ms is the back-to-back "
+                   "launch time including the binding's per-call cost")
+    return res
+
+
 def prefill_leg(args):
     import torch
     import bit_microscaled_flashattention_amd as mxa
@@ -894,6 +919,8 @@ def main():
             progress("hybrid leg done")
         if "tiny" in legs:
             line["tiny"] = tiny_leg(args)
+        if "quant" in legs:
+            line["quantize_jobs"] = quant_jobs_leg(args)
         print(json.dumps(line), flush=True)
         return
     pre, d, cal = prefill_leg(args)
