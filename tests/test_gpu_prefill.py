@@ -60,6 +60,18 @@ def test_gqa_ragged_tiles(kv_tile, causal):
     _run_case(q, k, v, causal=causal, kv_tile=kv_tile, what=f"gqa ragged tile={kv_tile}")
 
 
+def test_non_causal_gqa_whole_pairs_per_xcd_ragged():
+    """Non-causal launch whose (batch, KV head) pairs split evenly over the 8
+    XCDs, so each XCD runs one pair's query blocks after another: GQA group
+    of 4, a ragged query length (3 blocks, the last one partial) and a longer
+    key length, every row against the oracle."""
+    g = torch.Generator(device=DEV).manual_seed(23)
+    q = torch.randn((2, 16, 300, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((2, 4, 520, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((2, 4, 520, 128), generator=g, device=DEV).to(torch.bfloat16)
+    _run_case(q, k, v, causal=False, what="non-causal 8 pairs ragged")
+
+
 def test_rectangular_non_causal_d64_batch2():
     g = torch.Generator(device=DEV).manual_seed(22)
     q = torch.randn((2, 2, 200, 64), generator=g, device=DEV).to(torch.float16)
